@@ -1,0 +1,37 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def read_cases(name):
+    """Parse a tests/golden/*.txt fixture: '#' comments, 'case <name>' starts a
+    record, every other line is '<key> <values...>'."""
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            if key == "case":
+                cur = {"case": vals[0]}
+                cases.append(cur)
+            else:
+                cur[key] = vals
+    return cases
+
+
+@pytest.fixture(scope="session")
+def golden():
+    return read_cases

@@ -1,0 +1,316 @@
+"""Python binding of libaql.so, the MI355X (gfx950) per-output-channel INT8
+quantized linear.
+
+Argument marshalling only: every function checks dtypes, shapes and devices
+of torch tensors, allocates the outputs it was not given (torch.empty on the
+input's device), and calls the C entry point of the same name on the current
+torch stream. All arithmetic runs in the HIP kernels of libaql.so; there is no
+CPU or PyTorch fallback. A non-zero status raises AqlError with the library's
+message.
+
+The library is built in-tree (build.py, or __graft_entry__.build()); importing
+this package without it raises ImportError.
+"""
+import ctypes as C
+import os
+
+import torch  # loads the HIP runtime that libaql.so then shares (same soname)
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libaql.so")
+
+AQL_OK = 0
+AQL_ERR_NULL = -1
+AQL_ERR_SHAPE = -2
+AQL_ERR_ALIGN = -3
+AQL_ERR_PARAM = -4
+AQL_ERR_WORKSPACE = -5
+AQL_ERR_DEVICE = -6
+AQL_ERR_HIP = -7
+
+AQL_F32 = 0
+AQL_BF16 = 1
+AQL_WQ_SYM127 = 0
+AQL_WQ_SYM127_5 = 1
+AQL_W_Q8CSW = 0
+AQL_W_Q4GSW = 1
+AQL_OP_Q8TA_Q8CSW = 1
+AQL_OP_DQ8CA = 2
+AQL_MAX_K_INT8 = 65536
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run python -c 'import __graft_entry__ as g; "
+                      f"g.build()' (or python activation_quantized_linear_amd/build.py)")
+
+_lib = C.CDLL(LIB_PATH)
+
+_p = C.c_void_p
+_i64 = C.c_int64
+_i32 = C.c_int32
+_int = C.c_int
+_f32 = C.c_float
+_sz = C.c_size_t
+
+_SIGS = {
+    "aql_version": ([], C.c_int),
+    "aql_last_error": ([], C.c_char_p),
+    "aql_workspace_bytes": ([_int, _i64, _i64, _i64], _sz),
+    "aql_quantize_weight_int8": ([_p, _int, _i64, _i64, _int, _p, _p, _p, _p], _int),
+    "aql_quantize_weight_q4gsw": ([_p, _i64, _i64, _int, _p, _p, _p, _p], _int),
+    "aql_choose_qparams_rows": ([_p, _i64, _i64, _p, _p, _p, _p], _int),
+    "aql_quantize_act_per_tensor": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p, _p],
+                                    _int),
+    "aql_linear_w8a16": ([_p, _i64, _i64, _p, _p, _p, _i64, _p, _p], _int),
+    "aql_linear_q8ta_q8csw": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p, _p, _p,
+                               _i64, _p, _p, _sz, _p], _int),
+    "aql_linear_dq8ca": ([_p, _i64, _i64, _int, _p, _p, _p, _int, _p, _i64, _p, _p, _p, _p, _sz,
+                          _p], _int),
+    "aql_gemm_i8_i32": ([_p, _p, _p, _i64, _i64, _i64, _p], _int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class AqlError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def _check(fn, rc):
+    if rc != AQL_OK:
+        raise AqlError(fn, rc, aql_last_error())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return C.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _out(t, name, shape, dtype, dev):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _need(t, name, dtype, device=dev)
+    _shape(t, name, shape)
+    return t
+
+
+# ----------------------------------------------------------------- helpers
+
+
+def aql_version():
+    return _lib.aql_version()
+
+
+def aql_last_error():
+    return _lib.aql_last_error().decode()
+
+
+def aql_workspace_bytes(op, M, N, K):
+    return _lib.aql_workspace_bytes(op, M, N, K)
+
+
+# --------------------------------------------------------------- quantizers
+
+
+def aql_quantize_weight_int8(w, mode=AQL_WQ_SYM127, q=None, scale=None, wsum=None):
+    """w float32 or bfloat16 [N, K] -> (q int8 [N, K], scale float32 [N], wsum int32 [N])."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("w must be float32 or bfloat16")
+    _need(w, "w", w.dtype, 2)
+    N, K = w.shape
+    dev = w.device
+    q = _out(q, "q", (N, K), torch.int8, dev)
+    scale = _out(scale, "scale", (N,), torch.float32, dev)
+    wsum = _out(wsum, "wsum", (N,), torch.int32, dev)
+    dt = AQL_F32 if w.dtype == torch.float32 else AQL_BF16
+    _check("aql_quantize_weight_int8",
+           _lib.aql_quantize_weight_int8(_ptr(w), dt, N, K, mode, _ptr(q), _ptr(scale),
+                                         _ptr(wsum), _stream(dev)))
+    return q, scale, wsum
+
+
+def aql_quantize_weight_q4gsw(w, group=32, q4=None, gscale=None, gsum=None):
+    """w float32 [N, K] -> (q4 uint8 [N, K/2], gscale float32 [N, K/group], gsum int32 [N, K/group])."""
+    _need(w, "w", torch.float32, 2)
+    N, K = w.shape
+    if group <= 0 or K % group:
+        raise ValueError("K must be a multiple of group")
+    dev = w.device
+    q4 = _out(q4, "q4", (N, K // 2), torch.uint8, dev)
+    gscale = _out(gscale, "gscale", (N, K // group), torch.float32, dev)
+    gsum = _out(gsum, "gsum", (N, K // group), torch.int32, dev)
+    _check("aql_quantize_weight_q4gsw",
+           _lib.aql_quantize_weight_q4gsw(_ptr(w), N, K, group, _ptr(q4), _ptr(gscale),
+                                          _ptr(gsum), _stream(dev)))
+    return q4, gscale, gsum
+
+
+def aql_choose_qparams_rows(x, quantize=True, scale=None, zp=None, xq=None):
+    """x float32 [M, K] -> (scale float32 [M], zp int32 [M], xq int8 [M, K] or None)."""
+    _need(x, "x", torch.float32, 2)
+    M, K = x.shape
+    dev = x.device
+    scale = _out(scale, "scale", (M,), torch.float32, dev)
+    zp = _out(zp, "zp", (M,), torch.int32, dev)
+    if quantize:
+        xq = _out(xq, "xq", (M, K), torch.int8, dev)
+    _check("aql_choose_qparams_rows",
+           _lib.aql_choose_qparams_rows(_ptr(x), M, K, _ptr(scale), _ptr(zp),
+                                        _ptr(xq) if quantize else None, _stream(dev)))
+    return scale, zp, (xq if quantize else None)
+
+
+def aql_quantize_act_per_tensor(x, s1, z1, two_pass=False, s2=1.0, z2=0, xq1=None, xq2=None):
+    """x float32 [M, K] -> xq1 int8 [M, K] (and xq2 with two_pass)."""
+    _need(x, "x", torch.float32, 2)
+    M, K = x.shape
+    dev = x.device
+    xq1 = _out(xq1, "xq1", (M, K), torch.int8, dev)
+    if two_pass:
+        xq2 = _out(xq2, "xq2", (M, K), torch.int8, dev)
+    _check("aql_quantize_act_per_tensor",
+           _lib.aql_quantize_act_per_tensor(_ptr(x), M, K, float(s1), int(z1), int(bool(two_pass)),
+                                            float(s2), int(z2), _ptr(xq1),
+                                            _ptr(xq2) if two_pass else None, _stream(dev)))
+    return (xq1, xq2) if two_pass else xq1
+
+
+# -------------------------------------------------------------------- linears
+
+
+def aql_linear_w8a16(x, q, scale, bias=None, y=None):
+    """x bfloat16 [M, K], q int8 [N, K], scale float32 [N], bias bfloat16 [N] -> y bfloat16 [M, N]."""
+    _need(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    _need(q, "q", torch.int8, 2, dev)
+    M, K = x.shape
+    N = q.shape[0]
+    _shape(q, "q", (N, K))
+    _need(scale, "scale", torch.float32, 1, dev)
+    _shape(scale, "scale", (N,))
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, 1, dev)
+        _shape(bias, "bias", (N,))
+    y = _out(y, "y", (M, N), torch.bfloat16, dev)
+    _check("aql_linear_w8a16",
+           _lib.aql_linear_w8a16(_ptr(x), M, K, _ptr(q), _ptr(scale), _ptr(bias), N, _ptr(y),
+                                 _stream(dev)))
+    return y
+
+
+def _workspace(ws, nbytes, dev):
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(ws, "workspace", torch.uint8, device=dev)
+    return ws
+
+
+def aql_linear_q8ta_q8csw(x, s1, z1, q, wsum, wscale, bias=None, two_pass=False, s2=1.0, z2=0,
+                          y=None, workspace=None):
+    """Static per-tensor W8A8 linear (optional second pass). x float32 [M, K] -> y float32 [M, N]."""
+    _need(x, "x", torch.float32, 2)
+    dev = x.device
+    M, K = x.shape
+    _need(q, "q", torch.int8, 2, dev)
+    N = q.shape[0]
+    _shape(q, "q", (N, K))
+    _need(wsum, "wsum", torch.int32, 1, dev)
+    _shape(wsum, "wsum", (N,))
+    _need(wscale, "wscale", torch.float32, 1, dev)
+    _shape(wscale, "wscale", (N,))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, dev)
+        _shape(bias, "bias", (N,))
+    y = _out(y, "y", (M, N), torch.float32, dev)
+    nbytes = aql_workspace_bytes(AQL_OP_Q8TA_Q8CSW, M, N, K)
+    ws = _workspace(workspace, nbytes, dev)
+    _check("aql_linear_q8ta_q8csw",
+           _lib.aql_linear_q8ta_q8csw(_ptr(x), M, K, float(s1), int(z1), int(bool(two_pass)),
+                                      float(s2), int(z2), _ptr(q), _ptr(wsum), _ptr(wscale),
+                                      _ptr(bias), N, _ptr(y), _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+    return y
+
+
+def aql_linear_dq8ca(x, wq, wscale, wsum, wfmt=AQL_W_Q8CSW, group=0, bias=None, y=None,
+                     x_scale_out=None, x_zp_out=None, workspace=None):
+    """Dynamic per-row W8A8 linear. x float32 [M, K]; wq int8 [N, K] (Q8CSW) or uint8
+    [N, K/2] (Q4GSW) -> y float32 [M, N]. x_scale_out / x_zp_out, when given, receive
+    the per-row qparams."""
+    _need(x, "x", torch.float32, 2)
+    dev = x.device
+    M, K = x.shape
+    if wfmt == AQL_W_Q8CSW:
+        _need(wq, "wq", torch.int8, 2, dev)
+        N = wq.shape[0]
+        _shape(wq, "wq", (N, K))
+        sshape = (N,)
+    else:
+        _need(wq, "wq", torch.uint8, 2, dev)
+        N = wq.shape[0]
+        _shape(wq, "wq", (N, K // 2))
+        if group <= 0 or K % group:
+            raise ValueError("K must be a multiple of group")
+        sshape = (N, K // group)
+    _need(wscale, "wscale", torch.float32, len(sshape), dev)
+    _shape(wscale, "wscale", sshape)
+    _need(wsum, "wsum", torch.int32, len(sshape), dev)
+    _shape(wsum, "wsum", sshape)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, dev)
+        _shape(bias, "bias", (N,))
+    y = _out(y, "y", (M, N), torch.float32, dev)
+    if x_scale_out is not None:
+        x_scale_out = _out(x_scale_out, "x_scale_out", (M,), torch.float32, dev)
+    if x_zp_out is not None:
+        x_zp_out = _out(x_zp_out, "x_zp_out", (M,), torch.int32, dev)
+    nbytes = aql_workspace_bytes(AQL_OP_DQ8CA, M, N, K)
+    ws = _workspace(workspace, nbytes, dev)
+    _check("aql_linear_dq8ca",
+           _lib.aql_linear_dq8ca(_ptr(x), M, K, int(wfmt), _ptr(wq), _ptr(wscale), _ptr(wsum),
+                                 int(group), _ptr(bias), N, _ptr(y), _ptr(x_scale_out),
+                                 _ptr(x_zp_out), _ptr(ws), ws.numel(), _stream(dev)))
+    return y
+
+
+def aql_gemm_i8_i32(a, b, c=None):
+    """a int8 [M, K], b int8 [N, K] -> c int32 [M, N] = a @ b.T exactly."""
+    _need(a, "a", torch.int8, 2)
+    dev = a.device
+    _need(b, "b", torch.int8, 2, dev)
+    M, K = a.shape
+    N = b.shape[0]
+    _shape(b, "b", (N, K))
+    c = _out(c, "c", (M, N), torch.int32, dev)
+    _check("aql_gemm_i8_i32",
+           _lib.aql_gemm_i8_i32(_ptr(a), _ptr(b), _ptr(c), M, N, K, _stream(dev)))
+    return c

@@ -1,0 +1,330 @@
+// C ABI of libaql.so: argument validation, M-dispatch and launches.
+// Every check runs before the first HIP call, so an invalid call launches
+// nothing and touches no device state; an empty problem (M == 0 or N == 0)
+// returns AQL_OK without a HIP call.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "aql.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return AQL_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool finite_pos(float s) { return std::isfinite(s) && s > 0.0f; }
+
+bool z_ok(int32_t z) { return z >= -128 && z <= 127; }
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, 2 no.
+std::atomic<int> g_dev_ok[64];
+
+int check_device(const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return fail(AQL_ERR_DEVICE, "%s: no HIP device (%s)", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(AQL_ERR_DEVICE, "%s: device index %d out of range", fn, dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(AQL_ERR_DEVICE, "%s: hipGetDeviceProperties failed (%s)", fn,
+                  hipGetErrorString(e));
+    st = (std::string(prop.gcnArchName).rfind("gfx950", 0) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+    if (st == 2)
+      return fail(AQL_ERR_DEVICE, "%s: device %d is %s, this library is built for gfx950", fn,
+                  dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(AQL_ERR_DEVICE, "%s: device %d is not a gfx950", fn, dev);
+  return AQL_OK;
+}
+
+int launched(hipError_t e, const char *fn) {
+  if (e != hipSuccess) return fail(AQL_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+size_t ws_q8ta(int64_t M, int64_t K) { return 2 * align256((size_t)M * (size_t)K); }
+
+size_t ws_dq8ca(int64_t M, int64_t K) {
+  return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int aql_version(void) { return 100; }
+
+const char *aql_last_error(void) { return g_err.c_str(); }
+
+size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+  (void)N;
+  if (M < 0 || N < 0 || K < 0) return 0;
+  if (op == AQL_OP_Q8TA_Q8CSW) return ws_q8ta(M, K);
+  if (op == AQL_OP_DQ8CA) return ws_dq8ca(M, K);
+  return 0;
+}
+
+int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, int mode,
+                             int8_t *q, float *scale, int32_t *wsum, void *stream) {
+  const char *fn = "aql_quantize_weight_int8";
+  REQUIRE(w && q && scale, AQL_ERR_NULL, "%s: w, q and scale must not be NULL", fn);
+  REQUIRE(w_dtype == AQL_F32 || w_dtype == AQL_BF16, AQL_ERR_PARAM, "%s: unknown w_dtype %d", fn,
+          w_dtype);
+  REQUIRE(mode == AQL_WQ_SYM127 || mode == AQL_WQ_SYM127_5, AQL_ERR_PARAM, "%s: unknown mode %d",
+          fn, mode);
+  REQUIRE(N >= 0 && K >= 1 && K % 4 == 0, AQL_ERR_SHAPE,
+          "%s: need N >= 0, K >= 1 and K %% 4 == 0 (N=%lld K=%lld)", fn, (long long)N,
+          (long long)K);
+  REQUIRE(aligned16(w) && aligned16(q) && aligned16(scale) && aligned16(wsum), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (N == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_quantize_weight_int8(w, w_dtype == AQL_BF16, N, K, mode, q, scale,
+                                                   wsum, (hipStream_t)stream),
+                  fn);
+}
+
+int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, uint8_t *q4,
+                              float *gscale, int32_t *gsum, void *stream) {
+  const char *fn = "aql_quantize_weight_q4gsw";
+  REQUIRE(w && q4 && gscale, AQL_ERR_NULL, "%s: w, q4 and gscale must not be NULL", fn);
+  REQUIRE(group == 32, AQL_ERR_PARAM, "%s: group must be 32 (got %d)", fn, group);
+  REQUIRE(N >= 0 && K >= 32 && K % 32 == 0, AQL_ERR_SHAPE,
+          "%s: need N >= 0 and K a positive multiple of 32 (N=%lld K=%lld)", fn, (long long)N,
+          (long long)K);
+  REQUIRE(aligned16(w) && aligned16(q4) && aligned16(gscale) && aligned16(gsum), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (N == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_quantize_weight_q4gsw(w, N, K, q4, gscale, gsum,
+                                                    (hipStream_t)stream),
+                  fn);
+}
+
+int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
+                            int8_t *xq, void *stream) {
+  const char *fn = "aql_choose_qparams_rows";
+  REQUIRE(x && scale && zp, AQL_ERR_NULL, "%s: x, scale and zp must not be NULL", fn);
+  REQUIRE(M >= 0 && K >= 1 && K % 4 == 0, AQL_ERR_SHAPE,
+          "%s: need M >= 0, K >= 1 and K %% 4 == 0 (M=%lld K=%lld)", fn, (long long)M,
+          (long long)K);
+  REQUIRE(aligned16(x) && aligned16(scale) && aligned16(zp) && aligned16(xq), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  return launched(
+      aql::launch_choose_qparams_rows(x, M, K, scale, zp, xq, false, (hipStream_t)stream), fn);
+}
+
+int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                                int two_pass, float s2, int32_t z2, int8_t *xq1, int8_t *xq2,
+                                void *stream) {
+  const char *fn = "aql_quantize_act_per_tensor";
+  REQUIRE(x && xq1 && (!two_pass || xq2), AQL_ERR_NULL,
+          "%s: x, xq1 (and xq2 with two_pass) must not be NULL", fn);
+  REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
+          "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
+  REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
+          "%s: s2 must be finite and > 0, z2 in [-128, 127]", fn);
+  REQUIRE(M >= 0 && K >= 1 && K % 4 == 0, AQL_ERR_SHAPE,
+          "%s: need M >= 0, K >= 1 and K %% 4 == 0 (M=%lld K=%lld)", fn, (long long)M,
+          (long long)K);
+  REQUIRE(aligned16(x) && aligned16(xq1) && aligned16(xq2), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_quantize_act_per_tensor(x, M * K, s1, z1, two_pass != 0, s2, z2,
+                                                      xq1, xq2, (hipStream_t)stream),
+                  fn);
+}
+
+int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                     const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
+                     void *stream) {
+  const char *fn = "aql_linear_w8a16";
+  REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
+  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a positive multiple of 16 (M=%lld N=%lld K=%lld)", fn,
+          (long long)M, (long long)N, (long long)K);
+  REQUIRE(M <= 0xffff * 16LL && N <= 0x7fffffffLL * 16, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(x) && aligned16(q) && aligned16(scale) && aligned16(bias) && aligned16(y),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
+}
+
+int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                          int two_pass, float s2, int32_t z2, const int8_t *q,
+                          const int32_t *wsum, const float *wscale, const float *bias, int64_t N,
+                          float *y, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "aql_linear_q8ta_q8csw";
+  REQUIRE(x && q && wsum && wscale && y, AQL_ERR_NULL,
+          "%s: x, q, wsum, wscale and y must not be NULL", fn);
+  REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
+          "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
+  REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
+          "%s: s2 must be finite and > 0, z2 in [-128, 127]", fn);
+  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a multiple of 16 in [16, %d] (M=%lld N=%lld K=%lld)", fn,
+          AQL_MAX_K_INT8, (long long)M, (long long)N, (long long)K);
+  REQUIRE(M < (1LL << 31) / 128 && N < (1LL << 31) / 128, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(x) && aligned16(q) && aligned16(wsum) && aligned16(wscale) &&
+              aligned16(bias) && aligned16(y) && aligned16(ws),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return ok();
+  const size_t need = ws_q8ta(M, K);
+  REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
+          fn, need, ws ? ws_bytes : (size_t)0);
+  if (int e = check_device(fn)) return e;
+  int8_t *xq1 = static_cast<int8_t *>(ws);
+  int8_t *xq2 = xq1 + align256((size_t)M * (size_t)K);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = aql::launch_quantize_act_per_tensor(x, M * K, s1, z1, two_pass != 0, s2, z2, xq1,
+                                                     xq2, st);
+  if (e != hipSuccess) return launched(e, fn);
+  aql::GemmArgs a{};
+  a.a1 = xq1;
+  a.a2 = xq2;
+  a.b = q;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.wsum = wsum;
+  a.wscale = wscale;
+  a.bias = bias;
+  a.s1 = s1;
+  a.s2 = s2;
+  a.z1 = z1;
+  a.z2 = z2;
+  return launched(aql::launch_gemm_i8(a, aql::EPI_Q8TA, two_pass != 0, st), fn);
+}
+
+int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void *wq,
+                     const float *wscale, const int32_t *wsum, int group, const float *bias,
+                     int64_t N, float *y, float *x_scale_out, int32_t *x_zp_out, void *ws,
+                     size_t ws_bytes, void *stream) {
+  const char *fn = "aql_linear_dq8ca";
+  REQUIRE(x && wq && wscale && wsum && y, AQL_ERR_NULL,
+          "%s: x, wq, wscale, wsum and y must not be NULL", fn);
+  REQUIRE((wfmt == AQL_W_Q8CSW && group == 0) || (wfmt == AQL_W_Q4GSW && group == 32),
+          AQL_ERR_PARAM, "%s: wfmt/group must be Q8CSW/0 or Q4GSW/32 (got %d/%d)", fn, wfmt,
+          group);
+  const int64_t kmul = wfmt == AQL_W_Q4GSW ? 32 : 16;
+  REQUIRE(M >= 0 && N >= 0 && K >= kmul && K % kmul == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a multiple of %lld in [%lld, %d] (M=%lld N=%lld K=%lld)", fn,
+          (long long)kmul, (long long)kmul, AQL_MAX_K_INT8, (long long)M, (long long)N,
+          (long long)K);
+  REQUIRE(M < (1LL << 31) / 128 && N < (1LL << 31) / 128, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(x) && aligned16(wq) && aligned16(wscale) && aligned16(wsum) &&
+              aligned16(bias) && aligned16(y) && aligned16(x_scale_out) &&
+              aligned16(x_zp_out) && aligned16(ws),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return ok();
+  const size_t need = ws_dq8ca(M, K);
+  REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
+          fn, need, ws ? ws_bytes : (size_t)0);
+  if (int e = check_device(fn)) return e;
+  char *base = static_cast<char *>(ws);
+  int8_t *xq = reinterpret_cast<int8_t *>(base);
+  float *xs = x_scale_out ? x_scale_out
+                          : reinterpret_cast<float *>(base + align256((size_t)M * (size_t)K));
+  int32_t *xz = x_zp_out ? x_zp_out
+                         : reinterpret_cast<int32_t *>(base + align256((size_t)M * (size_t)K) +
+                                                       align256((size_t)M * 4));
+  hipStream_t st = (hipStream_t)stream;
+  const bool q4 = wfmt == AQL_W_Q4GSW;
+  hipError_t e = aql::launch_choose_qparams_rows(x, M, K, xs, xz, xq, q4, st);
+  if (e != hipSuccess) return launched(e, fn);
+  if (q4) {
+    aql::Q4Args a{};
+    a.xq = xq;
+    a.xs = xs;
+    a.xz = xz;
+    a.q4 = static_cast<const uint8_t *>(wq);
+    a.gs = wscale;
+    a.gsum = wsum;
+    a.bias = bias;
+    a.y = y;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    return launched(aql::launch_dq8ca_q4(a, st), fn);
+  }
+  aql::GemmArgs a{};
+  a.a1 = xq;
+  a.b = static_cast<const int8_t *>(wq);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.wsum = wsum;
+  a.wscale = wscale;
+  a.bias = bias;
+  a.xs = xs;
+  a.xz = xz;
+  return launched(aql::launch_gemm_i8(a, aql::EPI_DQ8, false, st), fn);
+}
+
+int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
+                    int64_t K, void *stream) {
+  const char *fn = "aql_gemm_i8_i32";
+  REQUIRE(a && b && c, AQL_ERR_NULL, "%s: a, b and c must not be NULL", fn);
+  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a multiple of 16 in [16, %d] (M=%lld N=%lld K=%lld)", fn,
+          AQL_MAX_K_INT8, (long long)M, (long long)N, (long long)K);
+  REQUIRE(M < (1LL << 31) / 128 && N < (1LL << 31) / 128, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(a) && aligned16(b) && aligned16(c), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return ok();
+  if (int e = check_device(fn)) return e;
+  aql::GemmArgs g{};
+  g.a1 = a;
+  g.b = b;
+  g.c = c;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return launched(aql::launch_gemm_i8(g, aql::EPI_RAW, false, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,368 @@
+// Quantizers: per-output-channel int8 weights, 4-bit group weights, static
+// per-tensor activations (one or two passes) and per-row asymmetric
+// activation qparams. All are HBM-bound streaming kernels: one read of the
+// float input, one write of the codes; a row that has to be reduced first
+// (absmax, min/max) is held in registers between the reduction and the
+// quantization so it is read from HBM once.
+#include "common.h"
+
+#include <float.h>
+
+namespace aql {
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void *p, int64_t idx) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + idx);
+    return make_float4(bf16_to_f32((uint16_t)(u.x & 0xffffu)), bf16_to_f32((uint16_t)(u.x >> 16)),
+                       bf16_to_f32((uint16_t)(u.y & 0xffffu)), bf16_to_f32((uint16_t)(u.y >> 16)));
+  } else {
+    return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + idx);
+  }
+}
+
+__device__ __forceinline__ float absmax4(float4 v) {
+  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+// ---------------------------------------------------------------- int8 weights
+// Ming INT8 linear quantize_weight / tiny-llm quantize_per_channel (den 127,
+// lo -127) and SmolVLM q8 recipe weight_int8 (den 127.5, lo -128):
+// q = clamp(rint(w / s), lo, 127) with s = absmax / den (1.0 for a zero row).
+
+__device__ __forceinline__ int wcode(float w, float s, float lo) {
+  return (int)clamp_code(rintf(w / s), lo, 127.0f);
+}
+
+// TPR threads own one row (TPR = 64: a wave per row, 4 rows per workgroup;
+// TPR = 256: the workgroup per row). VPT float4 vectors per thread stay in
+// registers between the absmax and the quantization; VPT = 0 re-reads the
+// row instead (rows longer than 16384).
+template <bool BF16, int TPR, int VPT>
+__global__ __launch_bounds__(256) void k_quantize_weight_int8(
+    const void *__restrict__ w, int64_t N, int64_t K, float den, float lo,
+    int8_t *__restrict__ q, float *__restrict__ scale, int32_t *__restrict__ wsum) {
+  __shared__ float red_f[4];
+  __shared__ int red_i[4];
+  constexpr int RPW = 256 / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t n = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const bool active = n < N;
+  const int64_t nvec = K >> 2;
+  const int64_t base = (active ? n : 0) * K;
+  uint32_t *qrow = reinterpret_cast<uint32_t *>(q + base);
+
+  float amax = 0.0f;
+  int sum = 0;
+  if constexpr (VPT > 0) {
+    float4 v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t j = t + (int64_t)i * TPR;
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && j < nvec) v[i] = load4<BF16>(w, base + 4 * j);
+      amax = fmaxf(amax, absmax4(v[i]));
+    }
+    amax = group_reduce_max<TPR>(amax, red_f);
+    const float s = (amax == 0.0f) ? 1.0f : amax / den;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t j = t + (int64_t)i * TPR;
+      if (active && j < nvec) {
+        const int a = wcode(v[i].x, s, lo), b = wcode(v[i].y, s, lo);
+        const int c = wcode(v[i].z, s, lo), d = wcode(v[i].w, s, lo);
+        qrow[j] = pack4(a, b, c, d);
+        sum += a + b + c + d;
+      }
+    }
+    sum = group_reduce_sum<TPR>(sum, red_i);
+    if (active && t == 0) {
+      scale[n] = s;
+      if (wsum) wsum[n] = sum;
+    }
+  } else {
+    for (int64_t j = t; j < nvec; j += TPR)
+      if (active) amax = fmaxf(amax, absmax4(load4<BF16>(w, base + 4 * j)));
+    amax = group_reduce_max<TPR>(amax, red_f);
+    const float s = (amax == 0.0f) ? 1.0f : amax / den;
+    for (int64_t j = t; j < nvec; j += TPR) {
+      if (!active) break;
+      const float4 v = load4<BF16>(w, base + 4 * j);
+      const int a = wcode(v.x, s, lo), b = wcode(v.y, s, lo);
+      const int c = wcode(v.z, s, lo), d = wcode(v.w, s, lo);
+      qrow[j] = pack4(a, b, c, d);
+      sum += a + b + c + d;
+    }
+    sum = group_reduce_sum<TPR>(sum, red_i);
+    if (active && t == 0) {
+      scale[n] = s;
+      if (wsum) wsum[n] = sum;
+    }
+  }
+}
+
+template <bool BF16>
+hipError_t quant_w8_dispatch(const void *w, int64_t N, int64_t K, float den, float lo, int8_t *q,
+                             float *scale, int32_t *wsum, hipStream_t st) {
+  const int64_t nvec = K / 4;
+  if (nvec <= 64 * 4) {
+    const dim3 grid((unsigned)((N + 3) / 4));
+    if (nvec <= 64)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 64, 1>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+    else if (nvec <= 128)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 64, 2>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+    else
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 64, 4>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+  } else {
+    const dim3 grid((unsigned)N);
+    if (nvec <= 256 * 2)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 256, 2>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+    else if (nvec <= 256 * 4)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 256, 4>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+    else if (nvec <= 256 * 8)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 256, 8>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+    else if (nvec <= 256 * 16)
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 256, 16>), grid, dim3(256), 0, st, w, N,
+                         K, den, lo, q, scale, wsum);
+    else
+      hipLaunchKernelGGL((k_quantize_weight_int8<BF16, 256, 0>), grid, dim3(256), 0, st, w, N, K,
+                         den, lo, q, scale, wsum);
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ q4gsw weights
+// One thread per (row, group of 32): gs = amax / 7.5 (1.0 for a zero group),
+// q4 = clamp(rint(w / gs), -8, 7), packed two per byte (k even low nibble).
+__global__ __launch_bounds__(256) void k_quantize_weight_q4gsw(
+    const float *__restrict__ w, int64_t N, int64_t K, uint8_t *__restrict__ q4,
+    float *__restrict__ gs, int32_t *__restrict__ gsum) {
+  const int64_t G = K / 32;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= N * G) return;
+  const int64_t n = id / G, g = id % G;
+  const float4 *src = reinterpret_cast<const float4 *>(w + n * K + g * 32);
+  float4 v[8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = src[i];
+    amax = fmaxf(amax, absmax4(v[i]));
+  }
+  const float s = (amax == 0.0f) ? 1.0f : amax / 7.5f;
+  uint32_t words[4];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float e[8] = {v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w,
+                        v[2 * i + 1].x, v[2 * i + 1].y, v[2 * i + 1].z, v[2 * i + 1].w};
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = (int)clamp_code(rintf(e[j] / s), -8.0f, 7.0f);
+      sum += c;
+      word |= (uint32_t)(c & 0xf) << (4 * j);
+    }
+    words[i] = word;
+  }
+  *reinterpret_cast<uint4 *>(q4 + n * (K / 2) + g * 16) =
+      make_uint4(words[0], words[1], words[2], words[3]);
+  gs[id] = s;
+  if (gsum) gsum[id] = sum;
+}
+
+// ------------------------------------------------------ per-tensor activations
+// SmolVLM q8 recipe fake_quant / Q8Linear.forward: xq = clamp(rint(x * inv) + z),
+// inv = 1/s; the two-pass residual r = x - (xq1 - z1) * s1 is a rounded
+// multiply followed by a rounded subtract (no FMA contraction).
+#pragma clang fp contract(off)
+__device__ __forceinline__ float act_code(float v, float inv, float z) {
+  return clamp_code(rintf(v * inv) + z, -128.0f, 127.0f);
+}
+
+template <bool TWO>
+__global__ __launch_bounds__(256) void k_quantize_act_per_tensor(
+    const float4 *__restrict__ x, int64_t nvec, float s1, float inv1, float z1, float inv2,
+    float z2, uint32_t *__restrict__ xq1, uint32_t *__restrict__ xq2) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    const float4 v = x[i];
+    const float a = act_code(v.x, inv1, z1), b = act_code(v.y, inv1, z1);
+    const float c = act_code(v.z, inv1, z1), d = act_code(v.w, inv1, z1);
+    xq1[i] = pack4((int)a, (int)b, (int)c, (int)d);
+    if constexpr (TWO) {
+      const float ra = v.x - (a - z1) * s1, rb = v.y - (b - z1) * s1;
+      const float rc = v.z - (c - z1) * s1, rd = v.w - (d - z1) * s1;
+      xq2[i] = pack4((int)act_code(ra, inv2, z2), (int)act_code(rb, inv2, z2),
+                     (int)act_code(rc, inv2, z2), (int)act_code(rd, inv2, z2));
+    }
+  }
+}
+
+// ------------------------------------------------------------ per-row qparams
+// ExecuTorch 8da4w choose_qparams_affine, read as the affine min/max rule:
+// mn = min(min x, 0), mx = max(max x, 0), s = max((mx - mn) / 255, eps),
+// zp = clamp(-128 - rint(mn / s)), then xq = clamp(rint(x * (1/s)) + zp).
+template <int TPR, int VPT, bool PERM>
+__global__ __launch_bounds__(256) void k_choose_qparams_rows(
+    const float *__restrict__ x, int64_t M, int64_t K, float *__restrict__ scale,
+    int32_t *__restrict__ zp, int8_t *__restrict__ xq) {
+  __shared__ float red_f[4];
+  constexpr int RPW = 256 / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t m = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
+  const bool active = m < M;
+  const int64_t nvec = K >> 2;
+  const int64_t base = (active ? m : 0) * K;
+  const float4 *row = reinterpret_cast<const float4 *>(x + base);
+
+  float mn = 0.0f, mx = 0.0f;
+  float4 v[VPT > 0 ? VPT : 1];
+  if constexpr (VPT > 0) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t j = t + (int64_t)i * TPR;
+      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active && j < nvec) v[i] = row[j];
+      mn = fminf(mn, fminf(fminf(v[i].x, v[i].y), fminf(v[i].z, v[i].w)));
+      mx = fmaxf(mx, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+    }
+  } else {
+    for (int64_t j = t; j < nvec; j += TPR) {
+      if (!active) break;
+      const float4 u = row[j];
+      mn = fminf(mn, fminf(fminf(u.x, u.y), fminf(u.z, u.w)));
+      mx = fmaxf(mx, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
+    }
+  }
+  mn = group_reduce_min<TPR>(mn, red_f);
+  mx = group_reduce_max<TPR>(mx, red_f);
+  const float s = fmaxf((mx - mn) / 255.0f, FLT_EPSILON);
+  const float zf = clamp_code(-128.0f - rintf(mn / s), -128.0f, 127.0f);
+  if (active && t == 0) {
+    scale[m] = s;
+    zp[m] = (int32_t)zf;
+  }
+  if (xq == nullptr || !active) return;
+  const float inv = 1.0f / s;
+  int8_t *out = xq + base;
+  auto emit = [&](int64_t j, float4 u) {
+    const int a = (int)act_code(u.x, inv, zf), b = (int)act_code(u.y, inv, zf);
+    const int c = (int)act_code(u.z, inv, zf), d = (int)act_code(u.w, inv, zf);
+    if constexpr (!PERM) {
+      reinterpret_cast<uint32_t *>(out)[j] = pack4(a, b, c, d);
+    } else {
+      // 8-k block stored as k = 0,2,4,6,1,3,5,7: the even half of the vector
+      // (k0..k3) fills bytes (0,1) and (4,5); the odd half (k4..k7) bytes (2,3), (6,7).
+      const int64_t blk = (j >> 1) * 8;
+      const int off = (j & 1) ? 2 : 0;
+      uint16_t *o16 = reinterpret_cast<uint16_t *>(out + blk + off);
+      o16[0] = (uint16_t)((a & 0xff) | ((c & 0xff) << 8));
+      o16[2] = (uint16_t)((b & 0xff) | ((d & 0xff) << 8));
+    }
+  };
+  if constexpr (VPT > 0) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int64_t j = t + (int64_t)i * TPR;
+      if (j < nvec) emit(j, v[i]);
+    }
+  } else {
+    for (int64_t j = t; j < nvec; j += TPR) emit(j, row[j]);
+  }
+}
+
+template <bool PERM>
+hipError_t cq_dispatch(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
+                       int8_t *xq, hipStream_t st) {
+  const int64_t nvec = K / 4;
+  if (nvec <= 64 * 4) {
+    const dim3 grid((unsigned)((M + 3) / 4));
+    if (nvec <= 64)
+      hipLaunchKernelGGL((k_choose_qparams_rows<64, 1, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+    else if (nvec <= 128)
+      hipLaunchKernelGGL((k_choose_qparams_rows<64, 2, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+    else
+      hipLaunchKernelGGL((k_choose_qparams_rows<64, 4, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+  } else {
+    const dim3 grid((unsigned)M);
+    if (nvec <= 256 * 2)
+      hipLaunchKernelGGL((k_choose_qparams_rows<256, 2, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+    else if (nvec <= 256 * 4)
+      hipLaunchKernelGGL((k_choose_qparams_rows<256, 4, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+    else if (nvec <= 256 * 8)
+      hipLaunchKernelGGL((k_choose_qparams_rows<256, 8, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+    else if (nvec <= 256 * 16)
+      hipLaunchKernelGGL((k_choose_qparams_rows<256, 16, PERM>), grid, dim3(256), 0, st, x, M,
+                         K, scale, zp, xq);
+    else
+      hipLaunchKernelGGL((k_choose_qparams_rows<256, 0, PERM>), grid, dim3(256), 0, st, x, M, K,
+                         scale, zp, xq);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_weight_int8(const void *w, bool bf16, int64_t N, int64_t K, int mode,
+                                       int8_t *q, float *scale, int32_t *wsum, hipStream_t st) {
+  const float den = mode == 0 ? 127.0f : 127.5f;
+  const float lo = mode == 0 ? -127.0f : -128.0f;
+  return bf16 ? quant_w8_dispatch<true>(w, N, K, den, lo, q, scale, wsum, st)
+              : quant_w8_dispatch<false>(w, N, K, den, lo, q, scale, wsum, st);
+}
+
+hipError_t launch_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, uint8_t *q4,
+                                        float *gs, int32_t *gsum, hipStream_t st) {
+  const int64_t items = N * (K / 32);
+  hipLaunchKernelGGL(k_quantize_weight_q4gsw, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                     st, w, N, K, q4, gs, gsum);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_act_per_tensor(const float *x, int64_t count, float s1, int32_t z1,
+                                          bool two_pass, float s2, int32_t z2, int8_t *xq1,
+                                          int8_t *xq2, hipStream_t st) {
+  const int64_t nvec = count / 4;
+  const float inv1 = 1.0f / s1;
+  const float inv2 = two_pass ? 1.0f / s2 : 0.0f;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  if (two_pass)
+    hipLaunchKernelGGL(k_quantize_act_per_tensor<true>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       reinterpret_cast<const float4 *>(x), nvec, s1, inv1, (float)z1, inv2,
+                       (float)z2, reinterpret_cast<uint32_t *>(xq1),
+                       reinterpret_cast<uint32_t *>(xq2));
+  else
+    hipLaunchKernelGGL(k_quantize_act_per_tensor<false>, dim3((unsigned)blocks), dim3(256), 0,
+                       st, reinterpret_cast<const float4 *>(x), nvec, s1, inv1, (float)z1, inv2,
+                       (float)z2, reinterpret_cast<uint32_t *>(xq1), nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale,
+                                      int32_t *zp, int8_t *xq, bool permute8, hipStream_t st) {
+  return permute8 ? cq_dispatch<true>(x, M, K, scale, zp, xq, st)
+                  : cq_dispatch<false>(x, M, K, scale, zp, xq, st);
+}
+
+}  // namespace aql

@@ -1,0 +1,390 @@
+#!/usr/bin/env python3
+"""Benchmark of the INT8 quantized linear on one MI355X; prints one JSON line.
+
+Headline (the metric's first half, on the SmolVLM-500M decode workload): one
+step is a full 32-layer decode sweep of the text decoder's MLP linears, 96
+W8A16 GEMVs (per layer up and gate [2560, 960], down [960, 2560], M = 1, bf16
+activations, int8 per-channel weights). The weights were quantized on the GPU
+beforehand (bind time, not timed). Three copies of the 32-layer weight set
+(712 MB, more than twice the 256 MB Infinity Cache) are rotated step by step
+so every step streams its weights from HBM; each copy's sweep is captured once
+in a HIP graph and replayed. value = algorithmic bytes of a sweep / time of a
+sweep, in GB/s (weights N*K + fp32 scales 4N + bf16 x 2MK + bf16 y 2MN per GEMV).
+
+Secondary rows (reported in "secondary"): the 7B-shape W8A16 GEMV/skinny GEMM
+(M = 1, 4, 16), the W8A8 static two-pass linear (M = 512, K = N = 4096; the
+metric's second half, TOPS against the int8 MFMA peak), the 8da4w dynamic
+linear, and the weight quantizer. Each is timed per call with HIP events on
+the stream the kernels run on, rotating enough weight copies to exceed the
+Infinity Cache.
+
+cpu_baseline: the CPU oracle (test infrastructure; its only use here) timed on
+the host on a bounded sample of the headline workload.
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A16 decode GEMV GB/s (% HBM peak); W8A8 prefill GEMM TOPS (% int8 MFMA)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="bound on the oracle's CPU time for cpu_baseline")
+    ap.add_argument("--only", default=None,
+                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant)")
+    return ap.parse_args()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(torch, fn, reps, rotate):
+    """Median of per-call durations (ms) from HIP events around each call."""
+    evs = []
+    for i in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i % rotate)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    d = [a.elapsed_time(b) for a, b in evs]
+    return statistics.median(d), d
+
+
+def copies_for(nbytes, minimum=2):
+    return max(minimum, -(-2 * MALL_BYTES // max(nbytes, 1)))
+
+
+# --------------------------------------------------------------- headline
+
+
+def sweep_workload(torch, aql, workloads, dev):
+    layers = workloads.smolvlm(seed=0)
+    base, xs = [], []
+    for L in layers:
+        e = {}
+        for wn in ("w_up", "w_gate", "w_down"):
+            q, s, _ = aql.aql_quantize_weight_int8(L[wn].to(dev), aql.AQL_WQ_SYM127)
+            e[wn] = (q, s)
+        xs.append((L["x_up"].to(dev), L["x_down"].to(dev)))
+        base.append(e)
+    torch.cuda.synchronize()
+    copies = 3
+    sets = [base] + [[{k: (v[0].clone(), v[1].clone()) for k, v in e.items()} for e in base]
+                     for _ in range(copies - 1)]
+    F, H = workloads.SMOLVLM_FFN, workloads.SMOLVLM_HIDDEN
+    ys = [(torch.empty(1, F, dtype=torch.bfloat16, device=dev),
+           torch.empty(1, F, dtype=torch.bfloat16, device=dev),
+           torch.empty(1, H, dtype=torch.bfloat16, device=dev)) for _ in layers]
+    calls = []
+    for c in range(copies):
+        cl = []
+        for li, e in enumerate(sets[c]):
+            xu, xd = xs[li]
+            yu, yg, yd = ys[li]
+            cl.append((xu, e["w_up"][0], e["w_up"][1], yu))
+            cl.append((xu, e["w_gate"][0], e["w_gate"][1], yg))
+            cl.append((xd, e["w_down"][0], e["w_down"][1], yd))
+        calls.append(cl)
+
+    def nbytes(x, q, y):
+        M, K = x.shape
+        N = q.shape[0]
+        return N * K + 4 * N + 2 * M * K + 2 * M * N
+
+    step_bytes = sum(nbytes(x, q, y) for x, q, s, y in calls[0])
+    return calls, step_bytes, nbytes, layers
+
+
+def run_sweep(torch, aql, dev, args, calls, step_bytes, nbytes):
+    def sweep(cl):
+        for x, q, s, y in cl:
+            aql.aql_linear_w8a16(x, q, s, None, y)
+
+    for cl in calls:  # eager warm-up (loads the code object)
+        sweep(cl)
+    torch.cuda.synchronize()
+    graphs = []
+    for cl in calls:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sweep(cl)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    say(f"sweep: {ms * 1e3:.1f} us/step, {step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+
+    # per-launch kernel durations (eager, events bracketing each launch)
+    per = []
+    tot_b = 0
+    for rep in range(3):
+        for cl in calls:
+            for x, q, s, y in cl:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                aql.aql_linear_w8a16(x, q, s, None, y)
+                b.record()
+                per.append((a, b, nbytes(x, q, y)))
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for a, b, _ in per]
+    tot_b = sum(nb for _, _, nb in per)
+    avg_ms = sum(durs) / len(durs)
+    achieved = tot_b / (sum(durs) * 1e-3) / 1e9
+    return ms, avg_ms, achieved, len(durs)
+
+
+# -------------------------------------------------------------- secondary
+
+
+def sec_llm7b(torch, aql, workloads, dev):
+    rows = []
+    for K, N in workloads.LLM7B_SHAPES:
+        d = workloads.llm7b(K, N, 1, seed=2)
+        q, s, _ = aql.aql_quantize_weight_int8(d["w"].to(dev), aql.AQL_WQ_SYM127)
+        del d
+        ncopy = copies_for(N * K)
+        qs = [q] + [q.clone() for _ in range(ncopy - 1)]
+        for M in (1, 4, 16):
+            x = workloads.llm7b(K, 16, M, seed=3)["x"].to(dev)
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
+            for i in range(ncopy):
+                fn(i)
+            med, _ = event_time_ms(torch, fn, 60, ncopy)
+            nb = N * K + 4 * N + 2 * M * K + 2 * M * N
+            gbs = nb / (med * 1e-3) / 1e9
+            rows.append({"workload": f"llm7b_w8a16 K={K} N={N} M={M}", "us": med * 1e3,
+                         "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                         "TFLOP/s": 2 * M * N * K / (med * 1e-3) / 1e12})
+            say(rows[-1])
+        del qs, q
+    return rows
+
+
+def sec_q8ta(torch, aql, workloads, dev):
+    d = workloads.two_pass(seed=0)
+    x = d["x"].to(dev)
+    calib = d["x"][d["calib_rows"]].reshape(1, -1).contiguous().to(dev)
+    sc, zc, _ = aql.aql_choose_qparams_rows(calib, quantize=False)
+    s1, z1 = float(sc.item()), int(zc.item())
+    import numpy as np
+    s2 = float(np.float32(s1) / np.float32(255.0))
+    q, ws, wsum = aql.aql_quantize_weight_int8(d["w"].to(dev), aql.AQL_WQ_SYM127_5)
+    M, K = x.shape
+    N = q.shape[0]
+    ncopy = copies_for(N * K + 8 * N)
+    qs = [(q, ws, wsum)] + [(q.clone(), ws.clone(), wsum.clone()) for _ in range(ncopy - 1)]
+    y = torch.empty(M, N, dtype=torch.float32, device=dev)
+    wsb = torch.empty(aql.aql_workspace_bytes(aql.AQL_OP_Q8TA_Q8CSW, M, N, K), dtype=torch.uint8,
+                      device=dev)
+    xq1 = torch.empty(M, K, dtype=torch.int8, device=dev)
+    xq2 = torch.empty(M, K, dtype=torch.int8, device=dev)
+    rows = []
+    for two in (True, False):
+        fn = lambda i: aql.aql_linear_q8ta_q8csw(x, s1, z1, qs[i][0], qs[i][2], qs[i][1], None,
+                                                 two, s2, 0, y, wsb)
+        for i in range(ncopy):
+            fn(i)
+        med, _ = event_time_ms(torch, fn, 60, ncopy)
+        pro = lambda i: aql.aql_quantize_act_per_tensor(x, s1, z1, two, s2, 0, xq1, xq2)
+        pmed, _ = event_time_ms(torch, pro, 30, 1)
+        ops = (2 if two else 1) * 2 * M * N * K
+        nb = 4 * M * K + N * K + 8 * N + 4 * M * N
+        gemm_ms = max(med - pmed, 1e-6)
+        rows.append({"workload": f"w8a8_q8ta {'two' if two else 'one'}-pass M={M} K={K} N={N}",
+                     "us": med * 1e3, "prologue_us": pmed * 1e3,
+                     "TOPS": ops / (med * 1e-3) / 1e12,
+                     "frac_int8": ops / (med * 1e-3) / 1e12 / INT8_PEAK_TOPS,
+                     "gemm_TOPS_est": ops / (gemm_ms * 1e-3) / 1e12,
+                     "GB/s": nb / (med * 1e-3) / 1e9})
+        say(rows[-1])
+    return rows
+
+
+def sec_dq8ca(torch, aql, workloads, dev):
+    rows = []
+    d = workloads.dyn8da4w(4, seed=0)
+    q4, gs, gsum = aql.aql_quantize_weight_q4gsw(d["w"].to(dev), 32)
+    N, K = q4.shape[0], q4.shape[1] * 2
+    wbytes = q4.numel() + 8 * gs.numel()
+    ncopy = copies_for(wbytes)
+    ws = [(q4, gs, gsum)] + [(q4.clone(), gs.clone(), gsum.clone()) for _ in range(ncopy - 1)]
+    for M in workloads.DYN_MS:
+        x = workloads.dyn8da4w(M, seed=1, N=16)["x"].to(dev)
+        y = torch.empty(M, N, dtype=torch.float32, device=dev)
+        wsb = torch.empty(aql.aql_workspace_bytes(aql.AQL_OP_DQ8CA, M, N, K), dtype=torch.uint8,
+                          device=dev)
+        fn = lambda i: aql.aql_linear_dq8ca(x, ws[i][0], ws[i][1], ws[i][2], aql.AQL_W_Q4GSW, 32,
+                                            None, y, workspace=wsb)
+        for i in range(ncopy):
+            fn(i)
+        med, _ = event_time_ms(torch, fn, 40, ncopy)
+        ops = 2 * M * N * K
+        nb = N * K // 2 + 4 * gs.numel() + 4 * M * K + 4 * M * N + 8 * M
+        rows.append({"workload": f"dq8ca_8da4w M={M} K={K} N={N}", "us": med * 1e3,
+                     "GB/s": nb / (med * 1e-3) / 1e9, "frac_hbm": nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "TOPS": ops / (med * 1e-3) / 1e12,
+                     "frac_int8": ops / (med * 1e-3) / 1e12 / INT8_PEAK_TOPS})
+        say(rows[-1])
+    return rows
+
+
+def sec_quant(torch, aql, workloads, dev):
+    K, N = 4096, 14336
+    w = workloads.llm7b(K, N, 1, seed=5)["w"].to(dev)
+    q = torch.empty(N, K, dtype=torch.int8, device=dev)
+    s = torch.empty(N, dtype=torch.float32, device=dev)
+    wsum = torch.empty(N, dtype=torch.int32, device=dev)
+    fn = lambda i: aql.aql_quantize_weight_int8(w, aql.AQL_WQ_SYM127, q, s, wsum)
+    fn(0)
+    med, _ = event_time_ms(torch, fn, 20, 1)
+    nb = 4 * N * K + N * K + 8 * N
+    row = {"workload": f"quantize_weight_int8 fp32 N={N} K={K}", "us": med * 1e3,
+           "GB/s": nb / (med * 1e-3) / 1e9, "frac_hbm": nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    say(row)
+    return [row]
+
+
+# ------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(layers, seconds):
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    prepared = []
+    for L in layers:
+        for wn, xn in (("w_up", "x_up"), ("w_gate", "x_up"), ("w_down", "x_down")):
+            q, s, _ = oracle.quantize_weight_int8(L[wn].numpy(), 0)
+            prepared.append((workloads.bf16_bits(L[xn]), q, s))
+    done_b, t0, gemvs = 0, time.perf_counter(), 0
+    while True:
+        for x, q, s in prepared:
+            oracle.linear_w8a16(x, q, s)
+            M, K = x.shape
+            N = q.shape[0]
+            done_b += N * K + 4 * N + 2 * M * K + 2 * M * N
+            gemvs += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done_b / el / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{gemvs} of the decode sweep's W8A16 GEMVs (in sweep order, fp64 sums), "
+                      f"{el:.1f} s on the host"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures a single GPU (got --gpus {args.gpus}, WORLD_SIZE {world}): the "
+              "quantized linear here runs on one MI355X, and no multi-GPU figure is produced.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import activation_quantized_linear_amd as aql
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    say(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    secondary = []
+    if args.only in (None, "sweep"):
+        calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
+        ms, avg_ms, achieved, nlaunch = run_sweep(torch, aql, dev, args, calls, step_bytes, nbytes)
+        del calls
+        torch.cuda.empty_cache()
+    if args.only is not None and args.only != "sweep":
+        fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant}[args.only]
+        print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
+        return
+    if not args.no_secondary:
+        for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant):
+            secondary += fn(torch, aql, workloads, dev)
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        say("cpu baseline ...")
+        cpu = cpu_baseline(layers, args.cpu_seconds)
+
+    value = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "smolvlm500m_decode_sweep: 32 layers x (up 2560x960, gate 2560x960, "
+                        "down 960x2560) W8A16 GEMVs, M=1, bf16 x, int8 per-channel weights, "
+                        "3 rotated weight copies (712 MB)",
+            "gemvs_per_step": 96,
+            "bytes_per_step": step_bytes,
+            "frac_hbm": value / HBM_PEAK_GBS,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "k_w8a16_skinny",
+            "avg_launch_us": avg_ms * 1e3,
+            "launches_timed": nlaunch,
+        },
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

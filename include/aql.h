@@ -1,0 +1,257 @@
+/*
+ * aql.h — C ABI of the MI355X (gfx950) per-output-channel INT8 quantized
+ * linear library (libaql.so).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named "device" are HIP device pointers owned by the caller. The
+ *   library never allocates, frees or synchronizes; every launch is ordered on
+ *   `stream` (a hipStream_t passed as void*, NULL = the legacy default stream)
+ *   and returns as soon as it is queued.
+ * - Matrices are row-major and contiguous. Weights are stored [N, K] =
+ *   [out_features, in_features], as the pages store a linear's weight.
+ * - Device base pointers must be 16-byte aligned (AQL_ERR_ALIGN otherwise).
+ * - bf16 values travel as their 16-bit patterns (uint16_t).
+ * - Every argument is validated before anything is launched; a rejected call
+ *   launches nothing and returns a negative status. aql_last_error() then
+ *   describes the first problem found (thread-local text). There is no silent
+ *   fallback to another algorithm or to the host.
+ * - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ * - Rounding: round-half-to-even everywhere a float becomes an integer code,
+ *   IEEE binary32 division where the definition divides, no flush of
+ *   subnormals. Integer results (codes, zero points, weight sums, int32
+ *   accumulators) are exact; float outputs carry fp32 rounding of the sums.
+ *
+ * Citations name the page and the section that defines the operation:
+ *   [SmolVLM q8 recipe]   SmolVLM-500M-Instruct ExecuTorch WebGPU 8-bit recipe
+ *                         building blocks (module docstring, weight_int8,
+ *                         fake_quant, Q8Linear, fix_q8ta_fake)
+ *   [Ming INT8 linear]    Ming-Image-0.1-Design-ROCm-INT8 int8_linear
+ *                         (QUANT_RULE, quantize_weight, Int8Linear)
+ *   [tiny-llm quant]      tiny-llm quant module (Step 4.6 docstring,
+ *                         quantize_per_channel, Int8Linear.forward)
+ *   [ExecuTorch PR 8da4w] ExecuTorch WebGPU PR "Add linear_dq8ca_q4gsw +
+ *                         choose_qparams_affine (8da4w)", Impl paragraph
+ *   [flashrt schemes]     flashrt-structures schemes, W8A16Decode
+ */
+#ifndef AQL_H_
+#define AQL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+#define AQL_OK 0
+#define AQL_ERR_NULL (-1)      /* a required pointer is NULL */
+#define AQL_ERR_SHAPE (-2)     /* a size is out of range or not a required multiple */
+#define AQL_ERR_ALIGN (-3)     /* a device base pointer is not 16-byte aligned */
+#define AQL_ERR_PARAM (-4)     /* a scale, zero point, mode, format or flag is invalid */
+#define AQL_ERR_WORKSPACE (-5) /* workspace missing or smaller than aql_workspace_bytes() */
+#define AQL_ERR_DEVICE (-6)    /* the current HIP device is not a gfx950 */
+#define AQL_ERR_HIP (-7)       /* a HIP call or launch failed (message kept) */
+
+/* ------------------------------------------------------------- enumerations */
+#define AQL_F32 0  /* float32 input */
+#define AQL_BF16 1 /* bfloat16 input (16-bit patterns) */
+
+#define AQL_WQ_SYM127 0   /* scale = absmax/127,   codes in [-127, 127] */
+#define AQL_WQ_SYM127_5 1 /* scale = absmax/127.5, codes in [-128, 127] */
+
+#define AQL_W_Q8CSW 0 /* int8 weights [N, K], one fp32 scale per output channel */
+#define AQL_W_Q4GSW 1 /* 4-bit group-symmetric weights, packed [N, K/2], fp32 scales [N, K/group] */
+
+#define AQL_OP_Q8TA_Q8CSW 1 /* workspace of aql_linear_q8ta_q8csw */
+#define AQL_OP_DQ8CA 2      /* workspace of aql_linear_dq8ca */
+
+/* Largest K accepted by the int8 paths: keeps |sum_k (xq - z) q| below 2^31. */
+#define AQL_MAX_K_INT8 65536
+
+/* ------------------------------------------------------------------ helpers */
+
+/* Library version, major*10000 + minor*100 + patch. Never fails. */
+int aql_version(void);
+
+/* Text describing the last failure on the calling thread ("" if none). The
+ * pointer stays valid until the next aql_* call on this thread. */
+const char *aql_last_error(void);
+
+/* Bytes of device workspace an operation needs for the given sizes (op is
+ * AQL_OP_*); 0 for an unknown op or negative sizes. Workspace contents need
+ * no initialization and are scratch after the call. */
+size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* ----------------------------------------------------------- quantizers */
+
+/*
+ * Per-output-channel symmetric int8 weight quantization.
+ * [Ming INT8 linear] QUANT_RULE / quantize_weight and [tiny-llm quant]
+ * quantize_per_channel (mode AQL_WQ_SYM127): scale[n] = max_k |w[n,k]| / 127,
+ * q = clamp(round(w / scale), -127, 127). [SmolVLM q8 recipe] weight_int8
+ * (mode AQL_WQ_SYM127_5): scale = absmax / 127.5, q = clamp(round(w /
+ * scale), -128, 127). An all-zero row gets scale 1.0 and q 0 in both modes.
+ *
+ *   w       device, [N, K] float32 (w_dtype AQL_F32) or bf16 (AQL_BF16)
+ *   q       device, [N, K] int8 codes (output)
+ *   scale   device, [N] float32 (output)
+ *   wsum    device, [N] int32 sum_k q[n,k] (output; may be NULL). This is the
+ *           weight_sums operand of the q8ta_q8csw op ([SmolVLM q8 recipe]
+ *           fix_q8ta_fake) and of aql_linear_dq8ca.
+ * Errors: NULL w/q/scale; N < 1 or K < 1 or K % 4 != 0 (f32) / K % 8 != 0 (bf16);
+ * unknown w_dtype or mode; misaligned pointers.
+ */
+int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, int mode,
+                             int8_t *q, float *scale, int32_t *wsum, void *stream);
+
+/*
+ * 4-bit group-symmetric weights for aql_linear_dq8ca (AQL_W_Q4GSW).
+ * [ExecuTorch PR 8da4w] consumes "4-bit group weights" with group scales but
+ * prints no producer or layout; the rule here is the symmetric observer rule
+ * of [SmolVLM q8 recipe] weight_int8 on the int4 range: per (n, group g)
+ * gs = amax_g / 7.5, q4 = clamp(round(w / gs), -8, 7), an all-zero group gets
+ * gs = 1 and q4 = 0.
+ *
+ *   w      device, [N, K] float32
+ *   q4     device, [N, K/2] bytes: byte n*K/2 + k/2 holds k even in the low
+ *          nibble and k odd in the high nibble, two's complement (output)
+ *   gscale device, [N, K/group] float32 (output)
+ *   gsum   device, [N, K/group] int32 sum of each group's codes (output; may be NULL)
+ * Errors: group must be 32; K % group != 0; N < 1; NULL or misaligned pointers.
+ */
+int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, uint8_t *q4,
+                              float *gscale, int32_t *gsum, void *stream);
+
+/*
+ * Per-row asymmetric int8 activation qparams, optionally fused with the
+ * quantization ([ExecuTorch PR 8da4w] choose_qparams_affine: per-row min/max,
+ * then scale and zero point; the rule is the affine min/max one of
+ * [SmolVLM q8 recipe] act_observer): mn = min(min_k x, 0),
+ * mx = max(max_k x, 0), scale = max((mx - mn) / 255, FLT_EPSILON),
+ * zp = clamp(-128 - round(mn / scale), -128, 127), and if xq is not NULL
+ * xq = clamp(round(x * (1/scale)) + zp, -128, 127).
+ *
+ *   x      device, [M, K] float32
+ *   scale  device, [M] float32 (output)
+ *   zp     device, [M] int32 holding values in [-128, 127] (output). The page
+ *          packs four int8 zero points per word to dodge a WebGPU write race;
+ *          here each row owns its own int32.
+ *   xq     device, [M, K] int8 (output; may be NULL)
+ * Errors: NULL x/scale/zp; M < 1, K < 1, K % 4 != 0; misaligned pointers.
+ */
+int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
+                            int8_t *xq, void *stream);
+
+/*
+ * Static per-tensor affine activation quantization, one or two passes: the
+ * prologue of aql_linear_q8ta_q8csw exposed as a stage.
+ * [SmolVLM q8 recipe] fake_quant / Q8Linear.forward:
+ * xq1 = clamp(round(x * (1/s1)) + z1, -128, 127); with two_pass,
+ * r = x - (xq1 - z1) * s1 (a rounded multiply, then a rounded subtract) and
+ * xq2 = clamp(round(r * (1/s2)) + z2, -128, 127).
+ *
+ *   x         device, [M, K] float32
+ *   xq1, xq2  device, [M, K] int8 (outputs; xq2 unused and may be NULL when
+ *             two_pass == 0)
+ * Errors: s1 (and s2 with two_pass) not finite and > 0; z outside [-128, 127];
+ * M < 1, K < 1, K % 4 != 0; NULL or misaligned pointers.
+ */
+int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                                int two_pass, float s2, int32_t z2, int8_t *xq1, int8_t *xq2,
+                                void *stream);
+
+/* --------------------------------------------------------------- linears */
+
+/*
+ * Weight-only W8A16 linear. [tiny-llm quant] Step 4.6 docstring and
+ * Int8Linear.forward: the per-channel scale factors out of the matmul,
+ * y[m, n] = scale[n] * sum_k x[m, k] * q[n, k] (+ bias[n]), int8 -> bf16 is
+ * exact (|q| <= 128 < 256). [Ming INT8 linear] Int8Linear keeps an optional
+ * bias. Decode-sized M runs a streaming kernel that reads the int8 rows
+ * once; larger M runs a tiled kernel ([flashrt schemes] W8A16Decode's
+ * M-dispatch; both branches are HIP).
+ *
+ *   x      device, [M, K] bf16
+ *   q      device, [N, K] int8 (from aql_quantize_weight_int8)
+ *   scale  device, [N] float32
+ *   bias   device, [N] bf16 (may be NULL)
+ *   y      device, [M, N] bf16, fp32 accumulate, round-to-nearest-even (output)
+ * Errors: NULL x/q/scale/y; M, N, K < 1; K % 16 != 0; misaligned pointers.
+ */
+int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                     const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
+                     void *stream);
+
+/*
+ * W8A8 linear with a static per-tensor affine activation scale and an
+ * optional second pass on the rounding residual (et_vk.linear_q8ta_q8csw of
+ * [SmolVLM q8 recipe], module docstring and Q8Linear.forward):
+ *   xq1 = q(x; s1, z1), r = x - dq(xq1), xq2 = q(r; s2, z2)
+ *   y[m, n] = wscale[n] * ( s1 * sum_k (xq1 - z1) q  +  s2 * sum_k (xq2 - z2) q ) + bias[n]
+ * with sum_k (xq - z) q = sum_k xq q - z * wsum[n] in exact int32, the same
+ * int8 weight for both passes, the bias added once.
+ *
+ *   x       device, [M, K] float32
+ *   q       device, [N, K] int8; wsum device [N] int32 = sum_k q[n, k];
+ *           wscale device [N] float32
+ *   bias    device, [N] float32 (may be NULL)
+ *   y       device, [M, N] float32 (output)
+ *   ws      device workspace of at least aql_workspace_bytes(AQL_OP_Q8TA_Q8CSW, M, N, K)
+ *           bytes; it receives the int8 codes xq1 [M, K] then xq2 [M, K].
+ * Errors: as aql_quantize_act_per_tensor, plus K % 64 != 0 or K > AQL_MAX_K_INT8,
+ * NULL q/wsum/wscale/y, workspace too small.
+ */
+int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                          int two_pass, float s2, int32_t z2, const int8_t *q,
+                          const int32_t *wsum, const float *wscale, const float *bias, int64_t N,
+                          float *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * W8A8 linear with dynamic per-row asymmetric int8 activations
+ * ([ExecuTorch PR 8da4w]: choose_qparams_affine, then linear_dq8ca with
+ * out[m, n] = s[m] * sum_k (xq[m, k] - z[m]) * dequant(w)[n, k]).
+ *   wfmt AQL_W_Q8CSW, group 0:  dequant(w) = q[n, k] * wscale[n];
+ *       y = s[m] * wscale[n] * (sum_k xq q - z[m] * wsum[n]) + bias[n]
+ *   wfmt AQL_W_Q4GSW, group 32: dequant(w) = q4[n, k] * wscale[n, k/32];
+ *       y = s[m] * sum_g wscale[n, g] * (sum_{k in g} xq q4 - z[m] * wsum[n, g]) + bias[n]
+ * Integer parts exact, group and output scaling in fp32. Any M >= 1 (the
+ * page's rows-multiple-of-4 limit does not apply).
+ *
+ *   x            device, [M, K] float32
+ *   wq           device, int8 [N, K] (Q8CSW) or packed q4 [N, K/2] (Q4GSW)
+ *   wscale       device, float32 [N] (Q8CSW) or [N, K/32] (Q4GSW)
+ *   wsum         device, int32 [N] or [N, K/32]: sums of the codes
+ *   bias         device, [N] float32 (may be NULL)
+ *   y            device, [M, N] float32 (output)
+ *   x_scale_out  device, [M] float32 (optional output: the row scales)
+ *   x_zp_out     device, [M] int32 (optional output: the row zero points)
+ *   ws           workspace of aql_workspace_bytes(AQL_OP_DQ8CA, M, N, K) bytes
+ * Errors: unknown wfmt or a group other than 0 (Q8CSW) / 32 (Q4GSW); K % 64 != 0
+ * or K > AQL_MAX_K_INT8; NULL or misaligned pointers; workspace too small.
+ */
+int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void *wq,
+                     const float *wscale, const int32_t *wsum, int group, const float *bias,
+                     int64_t N, float *y, float *x_scale_out, int32_t *x_zp_out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ stage entry */
+
+/*
+ * The int8 x int8 -> int32 contraction core of the W8A8 linears, exposed so
+ * that its accumulators can be checked bit for bit: c[m, n] = sum_k a[m, k] *
+ * b[n, k] (the integer sum inside [SmolVLM q8 recipe] Q8Linear's linear of
+ * dequantized operands, before any scale).
+ *
+ *   a  device, [M, K] int8;  b  device, [N, K] int8;  c  device, [M, N] int32 (output)
+ * Errors: M, N < 1; K < 64, K % 64 != 0 or K > AQL_MAX_K_INT8; NULL or misaligned pointers.
+ */
+int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
+                    int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQL_H_ */

@@ -1,0 +1,164 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/aql.h declares, and rejects every invalid argument with the documented
+status before making any HIP call (fake device addresses are never touched:
+validation fails first, or the problem is empty)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import activation_quantized_linear_amd as aql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aql.h")
+
+A = C.c_void_p(0x10000)      # a fake, 16-byte aligned address (never dereferenced)
+B = C.c_void_p(0x20000)
+Y = C.c_void_p(0x30000)
+MIS = C.c_void_p(0x10004)    # misaligned
+NUL = None
+L = aql._lib
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aql_\w+)\s*\(", text)))
+
+
+def test_header_and_exports_agree():
+    names = declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(aql.EXPORTED)
+
+
+def test_version_and_error_text():
+    assert aql.aql_version() >= 100
+    assert isinstance(aql.aql_last_error(), str)
+
+
+def test_workspace_bytes():
+    assert aql.aql_workspace_bytes(aql.AQL_OP_Q8TA_Q8CSW, 512, 4096, 4096) == 2 * 512 * 4096
+    assert aql.aql_workspace_bytes(aql.AQL_OP_DQ8CA, 4, 11008, 4096) >= 4 * 4096 + 8 * 4
+    assert aql.aql_workspace_bytes(99, 1, 1, 16) == 0
+    assert aql.aql_workspace_bytes(aql.AQL_OP_DQ8CA, -1, 1, 16) == 0
+
+
+def qw(*a):
+    return L.aql_quantize_weight_int8(*a, None)
+
+
+def test_quantize_weight_int8_validation():
+    assert qw(NUL, 0, 4, 16, 0, B, Y, None) == aql.AQL_ERR_NULL
+    assert qw(A, 0, 4, 16, 0, NUL, Y, None) == aql.AQL_ERR_NULL
+    assert qw(A, 2, 4, 16, 0, B, Y, None) == aql.AQL_ERR_PARAM
+    assert qw(A, 0, 4, 16, 2, B, Y, None) == aql.AQL_ERR_PARAM
+    assert qw(A, 0, 4, 0, 0, B, Y, None) == aql.AQL_ERR_SHAPE
+    assert qw(A, 0, 4, 18, 0, B, Y, None) == aql.AQL_ERR_SHAPE
+    assert qw(A, 0, -1, 16, 0, B, Y, None) == aql.AQL_ERR_SHAPE
+    assert qw(MIS, 0, 4, 16, 0, B, Y, None) == aql.AQL_ERR_ALIGN
+    assert qw(A, 0, 0, 16, 0, B, Y, None) == aql.AQL_OK  # empty: nothing launched
+    assert "K" in aql.aql_last_error() or aql.aql_last_error() == ""
+
+
+def test_q4gsw_validation():
+    f = L.aql_quantize_weight_q4gsw
+    assert f(NUL, 4, 64, 32, B, Y, None, None) == aql.AQL_ERR_NULL
+    assert f(A, 4, 64, 16, B, Y, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 48, 32, B, Y, None, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 4, 64, 32, MIS, Y, None, None) == aql.AQL_ERR_ALIGN
+    assert f(A, 0, 64, 32, B, Y, None, None) == aql.AQL_OK
+
+
+def test_choose_qparams_validation():
+    f = L.aql_choose_qparams_rows
+    assert f(NUL, 4, 64, B, Y, None, None) == aql.AQL_ERR_NULL
+    assert f(A, 4, 6, B, Y, None, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 4, 64, B, Y, MIS, None) == aql.AQL_ERR_ALIGN
+    assert f(A, 0, 64, B, Y, None, None) == aql.AQL_OK
+
+
+def test_act_quant_validation():
+    f = L.aql_quantize_act_per_tensor
+    assert f(A, 4, 64, 0.0, 0, 0, 1.0, 0, B, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 64, float("inf"), 0, 0, 1.0, 0, B, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 64, float("nan"), 0, 0, 1.0, 0, B, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 64, 0.1, 128, 0, 1.0, 0, B, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 64, 0.1, -129, 0, 1.0, 0, B, None, None) == aql.AQL_ERR_PARAM
+    assert f(A, 4, 64, 0.1, 0, 1, 1.0, 0, B, None, None) == aql.AQL_ERR_NULL
+    assert f(A, 4, 64, 0.1, 0, 1, -1.0, 0, B, Y, None) == aql.AQL_ERR_PARAM
+    assert f(A, 0, 64, 0.1, 0, 1, 0.01, 0, B, Y, None) == aql.AQL_OK
+
+
+def test_w8a16_validation():
+    f = L.aql_linear_w8a16
+    assert f(NUL, 1, 64, B, Y, None, 8, Y, None) == aql.AQL_ERR_NULL
+    assert f(A, 1, 64, B, Y, None, 8, NUL, None) == aql.AQL_ERR_NULL
+    assert f(A, 1, 40, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 1, 0, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
+    assert f(A, -1, 64, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 1, 64, B, Y, MIS, 8, Y, None) == aql.AQL_ERR_ALIGN
+    assert f(A, 0, 64, B, Y, None, 8, Y, None) == aql.AQL_OK
+    assert f(A, 3, 64, B, Y, None, 0, Y, None) == aql.AQL_OK
+
+
+def test_q8ta_validation():
+    f = L.aql_linear_q8ta_q8csw
+    args = lambda **k: [k.get("x", A), k.get("M", 4), k.get("K", 64), k.get("s1", 0.1),
+                        k.get("z1", 0), k.get("two", 1), k.get("s2", 0.001), k.get("z2", 0),
+                        k.get("q", B), k.get("wsum", Y), k.get("wsc", Y), None, k.get("N", 8),
+                        k.get("y", Y), k.get("ws", A), k.get("wsb", 1 << 20), None]
+    assert f(*args(q=NUL)) == aql.AQL_ERR_NULL
+    assert f(*args(wsum=NUL)) == aql.AQL_ERR_NULL
+    assert f(*args(s1=-0.1)) == aql.AQL_ERR_PARAM
+    assert f(*args(s2=0.0)) == aql.AQL_ERR_PARAM
+    assert f(*args(z2=300)) == aql.AQL_ERR_PARAM
+    assert f(*args(K=72)) == aql.AQL_ERR_SHAPE
+    assert f(*args(K=aql.AQL_MAX_K_INT8 + 16)) == aql.AQL_ERR_SHAPE
+    assert f(*args(y=MIS)) == aql.AQL_ERR_ALIGN
+    assert f(*args(wsb=100)) == aql.AQL_ERR_WORKSPACE
+    assert f(*args(ws=NUL)) == aql.AQL_ERR_WORKSPACE
+    assert f(*args(M=0)) == aql.AQL_OK
+
+
+def test_dq8ca_validation():
+    f = L.aql_linear_dq8ca
+    args = lambda **k: [A, k.get("M", 4), k.get("K", 64), k.get("wfmt", 0), B, Y, Y,
+                        k.get("group", 0), None, k.get("N", 8), k.get("y", Y), None, None,
+                        k.get("ws", A), k.get("wsb", 1 << 20), None]
+    assert f(*args(group=32)) == aql.AQL_ERR_PARAM
+    assert f(*args(wfmt=1, group=0)) == aql.AQL_ERR_PARAM
+    assert f(*args(wfmt=2)) == aql.AQL_ERR_PARAM
+    assert f(*args(wfmt=1, group=32, K=48)) == aql.AQL_ERR_SHAPE
+    assert f(*args(K=8)) == aql.AQL_ERR_SHAPE
+    assert f(*args(y=NUL)) == aql.AQL_ERR_NULL
+    assert f(*args(wsb=10)) == aql.AQL_ERR_WORKSPACE
+    assert f(*args(N=0)) == aql.AQL_OK
+
+
+def test_gemm_validation():
+    f = L.aql_gemm_i8_i32
+    assert f(NUL, B, Y, 4, 4, 64, None) == aql.AQL_ERR_NULL
+    assert f(A, B, Y, 4, 4, 24, None) == aql.AQL_ERR_SHAPE
+    assert f(A, B, MIS, 4, 4, 64, None) == aql.AQL_ERR_ALIGN
+    assert f(A, B, Y, 0, 4, 64, None) == aql.AQL_OK
+
+
+def test_valid_call_without_gpu_reports_device():
+    """On a host without a gfx950, a valid non-empty call fails with
+    AQL_ERR_DEVICE before launching anything."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = L.aql_gemm_i8_i32(A, B, Y, 4, 4, 64, None)
+    assert rc == aql.AQL_ERR_DEVICE
+    assert "device" in aql.aql_last_error().lower()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        aql.aql_gemm_i8_i32(torch.zeros(4, 64, dtype=torch.int8), torch.zeros(4, 64, dtype=torch.int8))

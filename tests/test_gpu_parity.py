@@ -1,0 +1,355 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same
+seeded inputs.
+
+Integer results (codes, scales of the quantizers, zero points, weight sums,
+int32 accumulators) must match bit for bit. Float outputs must satisfy, per
+element, |y - y_ref| <= rtol |y_ref| + atol * T, where T is the oracle's sum
+of the magnitudes of the addends (so cancellation near zero cannot fail a
+correct kernel), and, over the whole output, ||y - y_ref|| <= norm ||y_ref||:
+    fp32 outputs: rtol 1e-3, atol 1e-5, norm 1e-5
+    bf16 outputs: rtol 2e-2, atol 1e-4, norm 4e-3
+Sizes: small ragged shapes spanning several tiles with tails, the edge cases
+(empty, all-zero rows, one-sided rows, tiny scales, saturating outliers), and
+every workload at its full size, compared on all outputs where the oracle
+finishes in seconds and on sampled rows otherwise (rows are independent, so
+the oracle runs on the sampled rows only).
+"""
+import numpy as np
+import pytest
+import torch
+
+import activation_quantized_linear_amd as aql
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+FP32 = (1e-3, 1e-5, 1e-5)
+BF16 = (2e-2, 1e-4, 4e-3)
+
+
+def dev(t):
+    return t.contiguous().to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits(t):
+    return workloads.bf16_bits(t.cpu())
+
+
+def check_float(y, ref, tol, crit, what):
+    rtol, atol, norm = crit
+    y = np.asarray(y, np.float64)
+    assert y.shape == ref.shape, what
+    assert np.all(np.isfinite(y)), what
+    err = np.abs(y - ref)
+    bound = rtol * np.abs(ref) + atol * tol
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst at "
+                             f"{i}: got {y[i]!r} want {ref[i]!r} (T={tol[i]!r})")
+    den = max(np.linalg.norm(ref), 1e-300)
+    assert np.linalg.norm(y - ref) <= norm * den + 1e-300, f"{what}: normwise error too large"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ quantizers
+
+
+@pytest.mark.parametrize("mode", [aql.AQL_WQ_SYM127, aql.AQL_WQ_SYM127_5])
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+@pytest.mark.parametrize("N,K", [(256, 256), (37, 4), (5, 12), (70, 260), (9, 1028), (33, 4100),
+                                 (3, 17000), (130, 960)])
+def test_quantize_weight_int8(mode, wdt, N, K):
+    say("quantize_weight_int8", mode, wdt, N, K)
+    g = workloads.gen(100 + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    w[N // 2] = 0.0
+    if N > 3:
+        w[1] *= 1e-30  # subnormal-scale row
+        w[2, 0] = 5.0   # one outlier
+    if wdt == "bf16":
+        w = w.to(torch.bfloat16)
+    q, s, ws = aql.aql_quantize_weight_int8(dev(w), mode)
+    qo, so, wso = oracle.quantize_weight_int8(w.float().numpy(), mode)
+    assert np.array_equal(host(q), qo)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(ws), wso)
+
+
+def test_quantize_weight_tiny_zero_row():
+    d = workloads.tiny()
+    q, s, ws = aql.aql_quantize_weight_int8(dev(d["w"]), aql.AQL_WQ_SYM127)
+    qo, so, wso = oracle.quantize_weight_int8(d["w"].numpy(), 0)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    assert host(s)[7] == 1.0 and not host(q)[7].any() and host(ws)[7] == 0
+
+
+@pytest.mark.parametrize("K,N,mode", [(4096, 14336, 0), (14336, 4096, 0), (4096, 4096, 1)])
+def test_quantize_weight_full_size(K, N, mode):
+    say("quantize_weight full", K, N, mode)
+    d = workloads.llm7b(K, N, 1, seed=1)
+    q, s, ws = aql.aql_quantize_weight_int8(dev(d["w"]), mode)
+    qo, so, wso = oracle.quantize_weight_int8(d["w"].numpy(), mode)
+    assert np.array_equal(host(s), so)
+    assert np.array_equal(host(ws), wso)
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("N,K", [(7, 32), (33, 96), (100, 4096), (11008, 4096)])
+def test_quantize_weight_q4gsw(N, K):
+    say("q4gsw", N, K)
+    g = workloads.gen(200 + N)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    w[0, :32] = 0.0
+    q4, gs, gsum = aql.aql_quantize_weight_q4gsw(dev(w), 32)
+    q4o, gso, gsumo = oracle.quantize_weight_q4gsw(w.numpy(), 32)
+    assert np.array_equal(host(q4), q4o)
+    assert np.array_equal(host(gs), gso)
+    assert np.array_equal(host(gsum), gsumo)
+
+
+def _edge_rows(x):
+    M = x.shape[0]
+    if M >= 6:
+        x[1] = x[1].abs()
+        x[2] = -x[2].abs()
+        x[3] = 0.0
+        x[4] *= 1e-30
+        x[5, 1] = 3000.0
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(1, 4), (3, 100), (6, 256), (64, 4096), (2048, 4096), (5, 20000),
+                                 (9, 1028)])
+def test_choose_qparams_rows(M, K):
+    say("choose_qparams_rows", M, K)
+    g = workloads.gen(300 + M + K)
+    x = _edge_rows(workloads.small_matrix(g, M, K, std=2.0))
+    s, z, xq = aql.aql_choose_qparams_rows(dev(x))
+    so, zo, xqo = oracle.choose_qparams_rows(x.numpy())
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(z), zo)
+    assert np.array_equal(host(xq), xqo)
+    s2, z2, none = aql.aql_choose_qparams_rows(dev(x), quantize=False)
+    assert none is None and np.array_equal(host(s2), so) and np.array_equal(host(z2), zo)
+
+
+def test_per_tensor_calibration_as_one_row():
+    """The workload's static (s1, z1) is the per-row rule applied to all
+    calibration rows as one row; GPU and oracle agree bit for bit."""
+    d = workloads.two_pass()
+    calib = d["x"][d["calib_rows"]].reshape(1, -1).contiguous()
+    s, z, _ = aql.aql_choose_qparams_rows(dev(calib), quantize=False)
+    so, zo, _ = oracle.choose_qparams_rows(calib.numpy(), quantize=False)
+    assert host(s)[0] == so[0] and host(z)[0] == zo[0]
+
+
+@pytest.mark.parametrize("two_pass", [False, True])
+@pytest.mark.parametrize("M,K", [(1, 4), (37, 256), (512, 4096)])
+def test_quantize_act_per_tensor(two_pass, M, K):
+    say("quantize_act_per_tensor", two_pass, M, K)
+    d = workloads.two_pass(seed=7, M=max(M, 2), K=K, N=8)
+    x = d["x"][:M].contiguous()
+    s1, z1 = 0.0372, -3
+    s2, z2 = float(np.float32(s1) / np.float32(255.0)), 2
+    out = aql.aql_quantize_act_per_tensor(dev(x), s1, z1, two_pass, s2, z2)
+    ref = oracle.quantize_act_per_tensor(x.numpy(), s1, z1, two_pass, s2, z2)
+    if two_pass:
+        assert np.array_equal(host(out[0]), ref[0]) and np.array_equal(host(out[1]), ref[1])
+    else:
+        assert np.array_equal(host(out), ref)
+
+
+# ------------------------------------------------------------- integer GEMM
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (17, 33, 80), (130, 257, 272), (256, 256, 4096),
+                                   (3, 500, 64)])
+def test_gemm_i8_i32(M, N, K):
+    say("gemm_i8_i32", M, N, K)
+    rng = np.random.default_rng(M * 7 + N + K)
+    a = rng.integers(-128, 128, size=(M, K), dtype=np.int64).astype(np.int8)
+    b = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    a[0, :] = -128
+    b[0, :] = -128  # the largest products
+    c = aql.aql_gemm_i8_i32(dev(torch.from_numpy(a)), dev(torch.from_numpy(b)))
+    assert np.array_equal(host(c).astype(np.int64), oracle.gemm_i8(a, b))
+
+
+def test_gemm_i8_i32_full_size_sampled():
+    M, N, K = 512, 4096, 4096
+    say("gemm_i8_i32 full sampled", M, N, K)
+    rng = np.random.default_rng(9)
+    a = rng.integers(-128, 128, size=(M, K), dtype=np.int64).astype(np.int8)
+    b = rng.integers(-128, 128, size=(N, K), dtype=np.int64).astype(np.int8)
+    c = host(aql.aql_gemm_i8_i32(dev(torch.from_numpy(a)), dev(torch.from_numpy(b))))
+    rows = np.r_[0:4, 127:131, rng.choice(M, 8, replace=False), M - 1]
+    assert np.array_equal(c[rows].astype(np.int64), oracle.gemm_i8(a[rows], b))
+
+
+# -------------------------------------------------------------------- W8A16
+
+
+def _w8a16_case(x, w, bias=None):
+    q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+    b = None if bias is None else dev(bias)
+    y = aql.aql_linear_w8a16(dev(x), q, s, b)
+    yref, tol = oracle.linear_w8a16(bits(x), host(q), host(s),
+                                    None if bias is None else bits(bias))
+    return host(y.float()), yref, tol
+
+
+def test_w8a16_tiny():
+    d = workloads.tiny()
+    y, yref, tol = _w8a16_case(d["x"], d["w"])
+    check_float(y, yref, tol, BF16, "tiny")
+    assert np.all(y[:, 7] == 0.0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 15, 80), (1, 100, 960), (3, 33, 2560),
+                                   (16, 64, 4112), (17, 50, 128), (33, 129, 256), (70, 40, 1024)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a16_shapes(M, N, K, with_bias):
+    say("w8a16", M, N, K, with_bias)
+    g = workloads.gen(400 + M + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+    b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16) if with_bias else None
+    if N > 2:
+        w[1] = 0.0
+    y, yref, tol = _w8a16_case(x, w, b)
+    check_float(y, yref, tol, BF16, f"w8a16 {M}x{N}x{K}")
+
+
+def test_w8a16_smolvlm_sweep():
+    layers = workloads.smolvlm(seed=0)
+    say("w8a16 smolvlm sweep", len(layers))
+    for li, L in enumerate(layers):
+        for wname, xname in (("w_up", "x_up"), ("w_gate", "x_up"), ("w_down", "x_down")):
+            y, yref, tol = _w8a16_case(L[xname], L[wname])
+            check_float(y, yref, tol, BF16, f"layer {li} {wname}")
+
+
+@pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_w8a16_llm7b_full(K, N, M):
+    say("w8a16 7b", K, N, M)
+    d = workloads.llm7b(K, N, M, seed=2)
+    y, yref, tol = _w8a16_case(d["x"], d["w"])
+    check_float(y, yref, tol, BF16, f"7b {K}x{N} M={M}")
+
+
+# ------------------------------------------------------ W8A8 static two-pass
+
+
+def _calib(x_rows):
+    s, z, _ = oracle.choose_qparams_rows(np.ascontiguousarray(x_rows.reshape(1, -1)), quantize=False)
+    return float(s[0]), int(z[0])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 200, 256), (130, 129, 272), (64, 128, 1024)])
+@pytest.mark.parametrize("two_pass", [False, True])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_q8ta_shapes(M, N, K, two_pass, with_bias):
+    say("q8ta", M, N, K, two_pass, with_bias)
+    d = workloads.two_pass(seed=11 + M, M=max(M, 2), K=K, N=N)
+    x = d["x"][:M].contiguous()
+    s1, z1 = _calib(d["x"][1:].numpy())
+    s2 = float(np.float32(s1) / np.float32(255.0))
+    g = workloads.gen(500 + N)
+    b = workloads.small_matrix(g, 1, N)[0] if with_bias else None
+    q, ws, wsum = aql.aql_quantize_weight_int8(dev(d["w"]), aql.AQL_WQ_SYM127_5)
+    y = aql.aql_linear_q8ta_q8csw(dev(x), s1, z1, q, wsum, ws, None if b is None else dev(b),
+                                  two_pass, s2, 0)
+    o = oracle.linear_q8ta_q8csw(x.numpy(), s1, z1, host(q), host(ws),
+                                 None if b is None else b.numpy(), two_pass, s2, 0)
+    check_float(host(y), o["y"], o["tol"], FP32, "q8ta")
+
+
+def test_q8ta_two_pass_full_size_sampled():
+    d = workloads.two_pass()
+    x, w = d["x"], d["w"]
+    say("q8ta full", tuple(x.shape), tuple(w.shape))
+    s1, z1 = _calib(x[d["calib_rows"]].numpy())
+    s2 = float(np.float32(s1) / np.float32(255.0))
+    q, ws, wsum = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127_5)
+    qh, wsh, wsumh = host(q), host(ws), host(wsum)
+    qo, wso, wsumo = oracle.quantize_weight_int8(w.numpy(), 1)
+    assert np.array_equal(qh, qo) and np.array_equal(wsh, wso) and np.array_equal(wsumh, wsumo)
+    y = host(aql.aql_linear_q8ta_q8csw(dev(x), s1, z1, q, wsum, ws, None, True, s2, 0))
+    xq1, xq2 = aql.aql_quantize_act_per_tensor(dev(x), s1, z1, True, s2, 0)
+    r1, r2 = oracle.quantize_act_per_tensor(x.numpy(), s1, z1, True, s2, 0)
+    assert np.array_equal(host(xq1), r1) and np.array_equal(host(xq2), r2)
+    rng = np.random.default_rng(3)
+    rows = np.r_[0:2, rng.choice(np.arange(2, 512), 10, replace=False), 511]
+    o = oracle.linear_q8ta_q8csw(x.numpy()[rows], s1, z1, qh, wsh, None, True, s2, 0)
+    check_float(y[rows], o["y"], o["tol"], FP32, "q8ta full")
+    # the integer accumulators of both passes, through the stage entry
+    acc1 = host(aql.aql_gemm_i8_i32(xq1[rows[:4]].contiguous(), q))
+    assert np.array_equal(acc1.astype(np.int64), o["acc1"][:4])
+
+
+# ----------------------------------------------------- W8A8 dynamic (8da4w)
+
+
+def _dq8ca_case(x, w, wfmt, bias=None):
+    if wfmt == aql.AQL_W_Q8CSW:
+        wq, wsc, wsum = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        group = 0
+    else:
+        wq, wsc, wsum = aql.aql_quantize_weight_q4gsw(dev(w), 32)
+        group = 32
+    M = x.shape[0]
+    xs = torch.empty(M, dtype=torch.float32, device=DEV)
+    xz = torch.empty(M, dtype=torch.int32, device=DEV)
+    y = aql.aql_linear_dq8ca(dev(x), wq, wsc, wsum, wfmt, group,
+                             None if bias is None else dev(bias), x_scale_out=xs, x_zp_out=xz)
+    return host(y), host(wq), host(wsc), host(xs), host(xz), group
+
+
+@pytest.mark.parametrize("wfmt", [aql.AQL_W_Q8CSW, aql.AQL_W_Q4GSW])
+@pytest.mark.parametrize("M,N,K", [(1, 30, 64), (4, 100, 4096), (16, 17, 96), (17, 200, 256),
+                                   (128, 129, 512), (200, 64, 160)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
+    say("dq8ca", wfmt, M, N, K, with_bias)
+    g = workloads.gen(600 + M + N + K)
+    x = _edge_rows(workloads.small_matrix(g, M, K))
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    b = workloads.small_matrix(g, 1, N)[0] if with_bias else None
+    y, wq, wsc, xs, xz, group = _dq8ca_case(x, w, wfmt, b)
+    o = oracle.linear_dq8ca(x.numpy(), wq, wsc, wfmt, group, None if b is None else b.numpy())
+    assert np.array_equal(xs, o["x_scale"]) and np.array_equal(xz, o["x_zp"])
+    check_float(y, o["y"], o["tol"], FP32, f"dq8ca {wfmt} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", list(workloads.DYN_MS))
+def test_dq8ca_8da4w_full_size(M):
+    d = workloads.dyn8da4w(M, seed=4)
+    say("dq8ca 8da4w full", M)
+    x, w = d["x"], d["w"]
+    y, wq, wsc, xs, xz, _ = _dq8ca_case(x, w, aql.AQL_W_Q4GSW)
+    q4o, gso, _ = oracle.quantize_weight_q4gsw(w.numpy(), 32)
+    assert np.array_equal(wq, q4o) and np.array_equal(wsc, gso)
+    rng = np.random.default_rng(M)
+    rows = np.arange(M) if M <= 4 else np.r_[0:2, rng.choice(np.arange(2, M), 6, replace=False)]
+    o = oracle.linear_dq8ca(x.numpy()[rows], wq, wsc, oracle.W_Q4GSW, 32)
+    assert np.array_equal(xs[rows], o["x_scale"]) and np.array_equal(xz[rows], o["x_zp"])
+    check_float(y[rows], o["y"], o["tol"], FP32, f"8da4w M={M}")
+
+
+def test_empty_problems_are_noops():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros(8, 64, dtype=torch.int8, device=DEV)
+    s = torch.ones(8, dtype=torch.float32, device=DEV)
+    y = aql.aql_linear_w8a16(x, q, s)
+    assert tuple(y.shape) == (0, 8)

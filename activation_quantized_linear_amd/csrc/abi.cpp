@@ -1,7 +1,7 @@
 // C ABI of libaql.so: argument validation, M-dispatch and launches.
 // Every check runs before the first HIP call, so an invalid call launches
 // nothing and touches no device state; an empty problem (M == 0 or N == 0)
-// returns AQL_OK without a HIP call.
+// returns AQL_OK without a HIP call, and its (zero-element) buffers may be NULL.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -101,7 +101,6 @@ size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
 int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, int mode,
                              int8_t *q, float *scale, int32_t *wsum, void *stream) {
   const char *fn = "aql_quantize_weight_int8";
-  REQUIRE(w && q && scale, AQL_ERR_NULL, "%s: w, q and scale must not be NULL", fn);
   REQUIRE(w_dtype == AQL_F32 || w_dtype == AQL_BF16, AQL_ERR_PARAM, "%s: unknown w_dtype %d", fn,
           w_dtype);
   REQUIRE(mode == AQL_WQ_SYM127 || mode == AQL_WQ_SYM127_5, AQL_ERR_PARAM, "%s: unknown mode %d",
@@ -112,6 +111,7 @@ int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, i
   REQUIRE(aligned16(w) && aligned16(q) && aligned16(scale) && aligned16(wsum), AQL_ERR_ALIGN,
           "%s: pointers must be 16-byte aligned", fn);
   if (N == 0) return ok();
+  REQUIRE(w && q && scale, AQL_ERR_NULL, "%s: w, q and scale must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(aql::launch_quantize_weight_int8(w, w_dtype == AQL_BF16, N, K, mode, q, scale,
                                                    wsum, (hipStream_t)stream),
@@ -121,7 +121,6 @@ int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, i
 int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, uint8_t *q4,
                               float *gscale, int32_t *gsum, void *stream) {
   const char *fn = "aql_quantize_weight_q4gsw";
-  REQUIRE(w && q4 && gscale, AQL_ERR_NULL, "%s: w, q4 and gscale must not be NULL", fn);
   REQUIRE(group == 32, AQL_ERR_PARAM, "%s: group must be 32 (got %d)", fn, group);
   REQUIRE(N >= 0 && K >= 32 && K % 32 == 0, AQL_ERR_SHAPE,
           "%s: need N >= 0 and K a positive multiple of 32 (N=%lld K=%lld)", fn, (long long)N,
@@ -129,6 +128,7 @@ int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, u
   REQUIRE(aligned16(w) && aligned16(q4) && aligned16(gscale) && aligned16(gsum), AQL_ERR_ALIGN,
           "%s: pointers must be 16-byte aligned", fn);
   if (N == 0) return ok();
+  REQUIRE(w && q4 && gscale, AQL_ERR_NULL, "%s: w, q4 and gscale must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(aql::launch_quantize_weight_q4gsw(w, N, K, q4, gscale, gsum,
                                                     (hipStream_t)stream),
@@ -138,13 +138,13 @@ int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, u
 int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
                             int8_t *xq, void *stream) {
   const char *fn = "aql_choose_qparams_rows";
-  REQUIRE(x && scale && zp, AQL_ERR_NULL, "%s: x, scale and zp must not be NULL", fn);
   REQUIRE(M >= 0 && K >= 1 && K % 4 == 0, AQL_ERR_SHAPE,
           "%s: need M >= 0, K >= 1 and K %% 4 == 0 (M=%lld K=%lld)", fn, (long long)M,
           (long long)K);
   REQUIRE(aligned16(x) && aligned16(scale) && aligned16(zp) && aligned16(xq), AQL_ERR_ALIGN,
           "%s: pointers must be 16-byte aligned", fn);
   if (M == 0) return ok();
+  REQUIRE(x && scale && zp, AQL_ERR_NULL, "%s: x, scale and zp must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(
       aql::launch_choose_qparams_rows(x, M, K, scale, zp, xq, false, (hipStream_t)stream), fn);
@@ -154,8 +154,6 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
                                 int two_pass, float s2, int32_t z2, int8_t *xq1, int8_t *xq2,
                                 void *stream) {
   const char *fn = "aql_quantize_act_per_tensor";
-  REQUIRE(x && xq1 && (!two_pass || xq2), AQL_ERR_NULL,
-          "%s: x, xq1 (and xq2 with two_pass) must not be NULL", fn);
   REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
           "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
   REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
@@ -166,6 +164,8 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
   REQUIRE(aligned16(x) && aligned16(xq1) && aligned16(xq2), AQL_ERR_ALIGN,
           "%s: pointers must be 16-byte aligned", fn);
   if (M == 0) return ok();
+  REQUIRE(x && xq1 && (!two_pass || xq2), AQL_ERR_NULL,
+          "%s: x, xq1 (and xq2 with two_pass) must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(aql::launch_quantize_act_per_tensor(x, M * K, s1, z1, two_pass != 0, s2, z2,
                                                       xq1, xq2, (hipStream_t)stream),
@@ -176,7 +176,6 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                      void *stream) {
   const char *fn = "aql_linear_w8a16";
-  REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
   REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0, AQL_ERR_SHAPE,
           "%s: need M, N >= 0 and K a positive multiple of 16 (M=%lld N=%lld K=%lld)", fn,
           (long long)M, (long long)N, (long long)K);
@@ -185,6 +184,7 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
   REQUIRE(aligned16(x) && aligned16(q) && aligned16(scale) && aligned16(bias) && aligned16(y),
           AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
+  REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
 }
@@ -194,8 +194,6 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
                           const int32_t *wsum, const float *wscale, const float *bias, int64_t N,
                           float *y, void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "aql_linear_q8ta_q8csw";
-  REQUIRE(x && q && wsum && wscale && y, AQL_ERR_NULL,
-          "%s: x, q, wsum, wscale and y must not be NULL", fn);
   REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
           "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
   REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
@@ -209,6 +207,8 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
               aligned16(bias) && aligned16(y) && aligned16(ws),
           AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
+  REQUIRE(x && q && wsum && wscale && y, AQL_ERR_NULL,
+          "%s: x, q, wsum, wscale and y must not be NULL", fn);
   const size_t need = ws_q8ta(M, K);
   REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
           fn, need, ws ? ws_bytes : (size_t)0);
@@ -242,8 +242,6 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
                      int64_t N, float *y, float *x_scale_out, int32_t *x_zp_out, void *ws,
                      size_t ws_bytes, void *stream) {
   const char *fn = "aql_linear_dq8ca";
-  REQUIRE(x && wq && wscale && wsum && y, AQL_ERR_NULL,
-          "%s: x, wq, wscale, wsum and y must not be NULL", fn);
   REQUIRE((wfmt == AQL_W_Q8CSW && group == 0) || (wfmt == AQL_W_Q4GSW && group == 32),
           AQL_ERR_PARAM, "%s: wfmt/group must be Q8CSW/0 or Q4GSW/32 (got %d/%d)", fn, wfmt,
           group);
@@ -259,6 +257,8 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
               aligned16(x_zp_out) && aligned16(ws),
           AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
+  REQUIRE(x && wq && wscale && wsum && y, AQL_ERR_NULL,
+          "%s: x, wq, wscale, wsum and y must not be NULL", fn);
   const size_t need = ws_dq8ca(M, K);
   REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
           fn, need, ws ? ws_bytes : (size_t)0);
@@ -307,7 +307,6 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
 int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream) {
   const char *fn = "aql_gemm_i8_i32";
-  REQUIRE(a && b && c, AQL_ERR_NULL, "%s: a, b and c must not be NULL", fn);
   REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
           "%s: need M, N >= 0 and K a multiple of 16 in [16, %d] (M=%lld N=%lld K=%lld)", fn,
           AQL_MAX_K_INT8, (long long)M, (long long)N, (long long)K);
@@ -316,6 +315,7 @@ int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int
   REQUIRE(aligned16(a) && aligned16(b) && aligned16(c), AQL_ERR_ALIGN,
           "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
+  REQUIRE(a && b && c, AQL_ERR_NULL, "%s: a, b and c must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   aql::GemmArgs g{};
   g.a1 = a;

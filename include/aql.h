@@ -11,6 +11,9 @@
  * - Matrices are row-major and contiguous. Weights are stored [N, K] =
  *   [out_features, in_features], as the pages store a linear's weight.
  * - Device base pointers must be 16-byte aligned (AQL_ERR_ALIGN otherwise).
+ * - An empty problem (M == 0 or N == 0 where the function has them) is valid:
+ *   it returns AQL_OK without any HIP call, and pointers to its zero-element
+ *   buffers may be NULL. K must always be at least its stated minimum.
  * - bf16 values travel as their 16-bit patterns (uint16_t).
  * - Every argument is validated before anything is launched; a rejected call
  *   launches nothing and returns a negative status. aql_last_error() then
@@ -100,8 +103,8 @@ size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
  *   wsum    device, [N] int32 sum_k q[n,k] (output; may be NULL). This is the
  *           weight_sums operand of the q8ta_q8csw op ([SmolVLM q8 recipe]
  *           fix_q8ta_fake) and of aql_linear_dq8ca.
- * Errors: NULL w/q/scale; N < 1 or K < 1 or K % 4 != 0 (f32) / K % 8 != 0 (bf16);
- * unknown w_dtype or mode; misaligned pointers.
+ * Errors: NULL w/q/scale (N > 0); N < 0, K < 1 or K % 4 != 0; unknown w_dtype or
+ * mode; misaligned pointers.
  */
 int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, int mode,
                              int8_t *q, float *scale, int32_t *wsum, void *stream);
@@ -119,7 +122,8 @@ int aql_quantize_weight_int8(const void *w, int w_dtype, int64_t N, int64_t K, i
  *          nibble and k odd in the high nibble, two's complement (output)
  *   gscale device, [N, K/group] float32 (output)
  *   gsum   device, [N, K/group] int32 sum of each group's codes (output; may be NULL)
- * Errors: group must be 32; K % group != 0; N < 1; NULL or misaligned pointers.
+ * Errors: group must be 32; K < 32 or K % 32 != 0; N < 0; NULL (N > 0) or
+ * misaligned pointers.
  */
 int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, uint8_t *q4,
                               float *gscale, int32_t *gsum, void *stream);
@@ -139,7 +143,7 @@ int aql_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, int group, u
  *          packs four int8 zero points per word to dodge a WebGPU write race;
  *          here each row owns its own int32.
  *   xq     device, [M, K] int8 (output; may be NULL)
- * Errors: NULL x/scale/zp; M < 1, K < 1, K % 4 != 0; misaligned pointers.
+ * Errors: NULL x/scale/zp (M > 0); M < 0, K < 1, K % 4 != 0; misaligned pointers.
  */
 int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
                             int8_t *xq, void *stream);
@@ -156,7 +160,7 @@ int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, 
  *   xq1, xq2  device, [M, K] int8 (outputs; xq2 unused and may be NULL when
  *             two_pass == 0)
  * Errors: s1 (and s2 with two_pass) not finite and > 0; z outside [-128, 127];
- * M < 1, K < 1, K % 4 != 0; NULL or misaligned pointers.
+ * M < 0, K < 1, K % 4 != 0; NULL (M > 0) or misaligned pointers.
  */
 int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
                                 int two_pass, float s2, int32_t z2, int8_t *xq1, int8_t *xq2,
@@ -178,7 +182,8 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
  *   scale  device, [N] float32
  *   bias   device, [N] bf16 (may be NULL)
  *   y      device, [M, N] bf16, fp32 accumulate, round-to-nearest-even (output)
- * Errors: NULL x/q/scale/y; M, N, K < 1; K % 16 != 0; misaligned pointers.
+ * Errors: NULL x/q/scale/y (M, N > 0); M, N < 0; K < 16 or K % 16 != 0;
+ * misaligned pointers.
  */
 int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
@@ -200,7 +205,7 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
  *   y       device, [M, N] float32 (output)
  *   ws      device workspace of at least aql_workspace_bytes(AQL_OP_Q8TA_Q8CSW, M, N, K)
  *           bytes; it receives the int8 codes xq1 [M, K] then xq2 [M, K].
- * Errors: as aql_quantize_act_per_tensor, plus K % 64 != 0 or K > AQL_MAX_K_INT8,
+ * Errors: as aql_quantize_act_per_tensor, plus K < 16, K % 16 != 0 or K > AQL_MAX_K_INT8,
  * NULL q/wsum/wscale/y, workspace too small.
  */
 int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
@@ -228,7 +233,8 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
  *   x_scale_out  device, [M] float32 (optional output: the row scales)
  *   x_zp_out     device, [M] int32 (optional output: the row zero points)
  *   ws           workspace of aql_workspace_bytes(AQL_OP_DQ8CA, M, N, K) bytes
- * Errors: unknown wfmt or a group other than 0 (Q8CSW) / 32 (Q4GSW); K % 64 != 0
+ * Errors: unknown wfmt or a group other than 0 (Q8CSW) / 32 (Q4GSW); K not a
+ * positive multiple of 16 (Q8CSW) / 32 (Q4GSW)
  * or K > AQL_MAX_K_INT8; NULL or misaligned pointers; workspace too small.
  */
 int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void *wq,
@@ -245,7 +251,8 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
  * dequantized operands, before any scale).
  *
  *   a  device, [M, K] int8;  b  device, [N, K] int8;  c  device, [M, N] int32 (output)
- * Errors: M, N < 1; K < 64, K % 64 != 0 or K > AQL_MAX_K_INT8; NULL or misaligned pointers.
+ * Errors: M, N < 0; K < 16, K % 16 != 0 or K > AQL_MAX_K_INT8; NULL (M, N > 0) or
+ * misaligned pointers.
  */
 int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);

@@ -96,6 +96,7 @@ def two_pass(seed=0, M=512, K=4096, N=4096, n_outliers=8):
     """Static-activation workload with an attention-sink outlier row 0."""
     g = gen(seed)
     x = randn(g, M, K, std=4.0)
+    n_outliers = min(n_outliers, K)
     ch = torch.randperm(K, generator=g)[:n_outliers]
     mag = 2500.0 + 1000.0 * torch.rand(n_outliers, generator=g)
     sign = torch.where(torch.rand(n_outliers, generator=g) < 0.5, -1.0, 1.0)

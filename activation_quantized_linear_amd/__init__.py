@@ -66,6 +66,9 @@ _SIGS = {
     "aql_linear_dq8ca": ([_p, _i64, _i64, _int, _p, _p, _p, _int, _p, _i64, _p, _p, _p, _p, _sz,
                           _p], _int),
     "aql_gemm_i8_i32": ([_p, _p, _p, _i64, _i64, _i64, _p], _int),
+    "aql_w8a16_group_table_bytes": ([_int], _sz),
+    "aql_w8a16_group_plan": ([_p, _int, _p, _sz], _int),
+    "aql_linear_w8a16_grouped": ([_p, _p, _p], _int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -314,3 +317,55 @@ def aql_gemm_i8_i32(a, b, c=None):
     _check("aql_gemm_i8_i32",
            _lib.aql_gemm_i8_i32(_ptr(a), _ptr(b), _ptr(c), M, N, K, _stream(dev)))
     return c
+
+
+# ------------------------------------------------------------ grouped W8A16
+
+
+class _Problem(C.Structure):
+    _fields_ = [("x", _p), ("q", _p), ("scale", _p), ("bias", _p), ("y", _p),
+                ("M", _i64), ("N", _i64), ("K", _i64)]
+
+
+def aql_w8a16_group_table_bytes(count):
+    return _lib.aql_w8a16_group_table_bytes(count)
+
+
+def aql_w8a16_group_plan(problems):
+    """problems: sequence of (x, q, scale, bias or None, y) device tensors, each as
+    aql_linear_w8a16 takes them (y preallocated). Returns (host_table, dev_table):
+    the plan as a host uint8 tensor and its copy on the problems' device. Keep the
+    problems' tensors alive while the tables are in use."""
+    arr = (_Problem * len(problems))()
+    dev = None
+    for i, (x, q, scale, bias, y) in enumerate(problems):
+        _need(x, f"problems[{i}].x", torch.bfloat16, 2)
+        dev = x.device
+        _need(q, f"problems[{i}].q", torch.int8, 2, dev)
+        M, K = x.shape
+        N = q.shape[0]
+        _shape(q, f"problems[{i}].q", (N, K))
+        _need(scale, f"problems[{i}].scale", torch.float32, 1, dev)
+        _shape(scale, f"problems[{i}].scale", (N,))
+        if bias is not None:
+            _need(bias, f"problems[{i}].bias", torch.bfloat16, 1, dev)
+            _shape(bias, f"problems[{i}].bias", (N,))
+        _need(y, f"problems[{i}].y", torch.bfloat16, 2, dev)
+        _shape(y, f"problems[{i}].y", (M, N))
+        arr[i] = _Problem(x.data_ptr(), q.data_ptr(), scale.data_ptr(),
+                          0 if bias is None else bias.data_ptr(), y.data_ptr(), M, N, K)
+    nbytes = aql_w8a16_group_table_bytes(len(problems))
+    host = torch.empty(max(nbytes, 16), dtype=torch.uint8)
+    _check("aql_w8a16_group_plan",
+           _lib.aql_w8a16_group_plan(C.cast(arr, _p), len(problems), _ptr(host), host.numel()))
+    return host, host.to(dev)
+
+
+def aql_linear_w8a16_grouped(host_table, dev_table):
+    """Launch a planned group on the current stream of dev_table's device."""
+    if host_table.is_cuda or host_table.dtype != torch.uint8:
+        raise ValueError("host_table must be the host uint8 table from aql_w8a16_group_plan")
+    _need(dev_table, "dev_table", torch.uint8)
+    _check("aql_linear_w8a16_grouped",
+           _lib.aql_linear_w8a16_grouped(_ptr(host_table), _ptr(dev_table),
+                                         _stream(dev_table.device)))

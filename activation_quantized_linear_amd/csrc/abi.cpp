@@ -82,6 +82,37 @@ size_t ws_dq8ca(int64_t M, int64_t K) {
   return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
 }
 
+// Largest K of the W8A16 kernels: a 16-row tile of x (bf16) stays below the
+// out-of-range offset its buffer loads use.
+constexpr int64_t kMaxKW8A16 = 1 << 24;
+
+// Host table of a grouped W8A16 launch: this header, then one entry per
+// non-empty problem.
+struct GroupHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t count;         // entries that follow (non-empty problems)
+  int32_t total_blocks;  // grid size
+  int32_t waves;         // waves per workgroup
+  int32_t reserved[11];
+};
+static_assert(sizeof(GroupHeader) == 64, "table header");
+constexpr uint32_t kGroupMagic = 0x47514c41u;  // "ALQG"
+
+int check_w8a16(const char *fn, const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                const float *scale, const uint16_t *bias, int64_t N, const uint16_t *y) {
+  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= kMaxKW8A16, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a multiple of 16 in [16, %lld] (M=%lld N=%lld K=%lld)", fn,
+          (long long)kMaxKW8A16, (long long)M, (long long)N, (long long)K);
+  REQUIRE(M <= 0xffff * 16LL && N <= 0x7fffffffLL * 16, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(x) && aligned16(q) && aligned16(scale) && aligned16(bias) && aligned16(y),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return AQL_OK;
+  REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
+  return AQL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -176,17 +207,78 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                      void *stream) {
   const char *fn = "aql_linear_w8a16";
-  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0, AQL_ERR_SHAPE,
-          "%s: need M, N >= 0 and K a positive multiple of 16 (M=%lld N=%lld K=%lld)", fn,
-          (long long)M, (long long)N, (long long)K);
-  REQUIRE(M <= 0xffff * 16LL && N <= 0x7fffffffLL * 16, AQL_ERR_SHAPE, "%s: M or N too large",
-          fn);
-  REQUIRE(aligned16(x) && aligned16(q) && aligned16(scale) && aligned16(bias) && aligned16(y),
-          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (int e = check_w8a16(fn, x, M, K, q, scale, bias, N, y)) return e;
   if (M == 0 || N == 0) return ok();
-  REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
+}
+
+size_t aql_w8a16_group_table_bytes(int count) {
+  if (count < 1) return 0;
+  return sizeof(GroupHeader) + (size_t)count * sizeof(aql::W8A16GroupEntry);
+}
+
+int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *table,
+                         size_t table_bytes) {
+  const char *fn = "aql_w8a16_group_plan";
+  REQUIRE(count >= 1, AQL_ERR_SHAPE, "%s: count must be >= 1 (got %d)", fn, count);
+  REQUIRE(problems, AQL_ERR_NULL, "%s: problems must not be NULL", fn);
+  REQUIRE(table && table_bytes >= aql_w8a16_group_table_bytes(count), AQL_ERR_WORKSPACE,
+          "%s: table needs %zu bytes", fn, aql_w8a16_group_table_bytes(count));
+  GroupHeader *h = static_cast<GroupHeader *>(table);
+  aql::W8A16GroupEntry *e = reinterpret_cast<aql::W8A16GroupEntry *>(h + 1);
+  int64_t blocks = 0, kmin = 0;
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const aql_w8a16_problem &p = problems[i];
+    char name[64];
+    snprintf(name, sizeof name, "%s: problem %d", fn, i);
+    if (int rc = check_w8a16(name, p.x, p.M, p.K, p.q, p.scale, p.bias, p.N, p.y)) return rc;
+    if (p.M == 0 || p.N == 0) continue;
+    const int64_t nblk = (p.N + 15) / 16, mblk = (p.M + 15) / 16;
+    REQUIRE(blocks + nblk * mblk <= 0x7fffffffLL, AQL_ERR_SHAPE, "%s: too many tiles in total",
+            fn);
+    aql::W8A16GroupEntry &d = e[n++];
+    d = aql::W8A16GroupEntry{};
+    d.x = p.x;
+    d.q = p.q;
+    d.scale = p.scale;
+    d.bias = p.bias;
+    d.y = p.y;
+    d.M = p.M;
+    d.N = p.N;
+    d.K = p.K;
+    d.blk_begin = (int32_t)blocks;
+    d.nblk = (int32_t)nblk;
+    blocks += nblk * mblk;
+    kmin = (kmin == 0 || p.K < kmin) ? p.K : kmin;
+  }
+  *h = GroupHeader{};
+  h->magic = kGroupMagic;
+  h->version = 1;
+  h->count = n;
+  h->total_blocks = (int32_t)blocks;
+  int w = n ? aql::w8a16_waves(kmin, blocks) : 1;
+  h->waves = w > 8 ? 8 : w;
+  return ok();
+}
+
+int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *stream) {
+  const char *fn = "aql_linear_w8a16_grouped";
+  REQUIRE(table, AQL_ERR_NULL, "%s: table must not be NULL", fn);
+  const GroupHeader *h = static_cast<const GroupHeader *>(table);
+  REQUIRE(h->magic == kGroupMagic && h->version == 1 && h->count >= 0 && h->total_blocks >= 0 &&
+              (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8),
+          AQL_ERR_PARAM, "%s: table was not written by aql_w8a16_group_plan", fn);
+  if (h->count == 0 || h->total_blocks == 0) return ok();
+  REQUIRE(dev_table, AQL_ERR_NULL, "%s: dev_table must not be NULL", fn);
+  REQUIRE(aligned16(dev_table), AQL_ERR_ALIGN, "%s: dev_table must be 16-byte aligned", fn);
+  if (int e = check_device(fn)) return e;
+  const aql::W8A16GroupEntry *dev_entries = reinterpret_cast<const aql::W8A16GroupEntry *>(
+      static_cast<const char *>(dev_table) + sizeof(GroupHeader));
+  return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, h->waves,
+                                            (hipStream_t)stream),
+                  fn);
 }
 
 int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_t z1,

@@ -42,6 +42,26 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st);
 
+// Waves per workgroup the W8A16 kernel uses for K and a grid of `blocks` tiles.
+int w8a16_waves(int64_t K, int64_t blocks);
+
+// One problem of a grouped W8A16 launch, as stored in the device table.
+struct W8A16GroupEntry {
+  const uint16_t *x;
+  const int8_t *q;
+  const float *scale;
+  const uint16_t *bias;
+  uint16_t *y;
+  int64_t M, N, K;
+  int32_t blk_begin;  // first grid block of this problem
+  int32_t nblk;       // 16-channel blocks along N
+  int32_t pad[2];
+};
+static_assert(sizeof(W8A16GroupEntry) == 80, "table layout");
+
+hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
+                                int waves, hipStream_t st);
+
 // int8 GEMM epilogues
 enum GemmEpi { EPI_RAW = 0, EPI_Q8TA = 1, EPI_DQ8 = 2 };
 

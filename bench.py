@@ -5,18 +5,20 @@ Headline (the metric's first half, on the SmolVLM-500M decode workload): one
 step is a full 32-layer decode sweep of the text decoder's MLP linears, 96
 W8A16 GEMVs (per layer up and gate [2560, 960], down [960, 2560], M = 1, bf16
 activations, int8 per-channel weights). The weights were quantized on the GPU
-beforehand (bind time, not timed). Three copies of the 32-layer weight set
-(712 MB, more than twice the 256 MB Infinity Cache) are rotated step by step
-so every step streams its weights from HBM; each copy's sweep is captured once
-in a HIP graph and replayed. value = algorithmic bytes of a sweep / time of a
-sweep, in GB/s (weights N*K + fp32 scales 4N + bf16 x 2MK + bf16 y 2MN per GEMV).
+beforehand (bind time, not timed). The layers' linears do not feed one
+another, so a step is one grouped launch over all 96 (planned once per weight
+copy). Three copies of the 32-layer weight set (712 MB, more than twice the
+256 MB Infinity Cache) are rotated step by step so every step streams its
+weights from HBM. value = algorithmic bytes of a sweep / time of a sweep, in
+GB/s (weights N*K + fp32 scales 4N + bf16 x 2MK + bf16 y 2MN per GEMV). The
+same sweep as 96 separate launches in a HIP graph is a secondary row.
 
 Secondary rows (reported in "secondary"): the 7B-shape W8A16 GEMV/skinny GEMM
 (M = 1, 4, 16), the W8A8 static two-pass linear (M = 512, K = N = 4096; the
 metric's second half, TOPS against the int8 MFMA peak), the 8da4w dynamic
-linear, and the weight quantizer. Each is timed per call with HIP events on
-the stream the kernels run on, rotating enough weight copies to exceed the
-Infinity Cache.
+linear, and the weight quantizer. Each is timed with HIP events on the stream
+the kernels run on, bracketing a run of back-to-back calls that rotates enough
+weight copies to exceed the Infinity Cache.
 
 cpu_baseline: the CPU oracle (test infrastructure; its only use here) timed on
 the host on a bounded sample of the headline workload.
@@ -56,19 +58,20 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def event_time_ms(torch, fn, reps, rotate):
-    """Median of per-call durations (ms) from HIP events around each call."""
-    evs = []
-    for i in range(reps):
+def event_time_ms(torch, fn, reps, rotate, trials=5):
+    """Per-call time (ms): HIP events bracket `reps` back-to-back calls on the
+    current stream (rotating over `rotate` buffer sets); median of `trials`."""
+    res = []
+    for _ in range(trials):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        fn(i % rotate)
+        for i in range(reps):
+            fn(i % rotate)
         b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    d = [a.elapsed_time(b) for a, b in evs]
-    return statistics.median(d), d
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) / reps)
+    return statistics.median(res), res
 
 
 def copies_for(nbytes, minimum=2):
@@ -116,12 +119,37 @@ def sweep_workload(torch, aql, workloads, dev):
     return calls, step_bytes, nbytes, layers
 
 
-def run_sweep(torch, aql, dev, args, calls, step_bytes, nbytes):
+def run_sweep(torch, aql, dev, args, calls, step_bytes):
+    """Headline: each step is one grouped launch over the 96 GEMVs of one weight
+    copy; the timed region is bracketed by HIP events on the launch stream, so
+    its average is the grouped kernel's average launch duration."""
+    plans = [aql.aql_w8a16_group_plan([(x, q, s, None, y) for x, q, s, y in cl]) for cl in calls]
+    for h, d in plans:
+        aql.aql_linear_w8a16_grouped(h, d)
+    for i in range(args.warmup):
+        h, d = plans[i % len(plans)]
+        aql.aql_linear_w8a16_grouped(h, d)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        h, d = plans[i % len(plans)]
+        aql.aql_linear_w8a16_grouped(h, d)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    say(f"sweep (grouped): {ms * 1e3:.1f} us/step, {step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+    return ms
+
+
+def sweep_as_graph(torch, aql, calls, step_bytes, reps=60):
+    """Secondary row: the same sweep as 96 separate launches captured in a HIP graph."""
     def sweep(cl):
         for x, q, s, y in cl:
             aql.aql_linear_w8a16(x, q, s, None, y)
 
-    for cl in calls:  # eager warm-up (loads the code object)
+    for cl in calls:
         sweep(cl)
     torch.cuda.synchronize()
     graphs = []
@@ -130,38 +158,12 @@ def run_sweep(torch, aql, dev, args, calls, step_bytes, nbytes):
         with torch.cuda.graph(g):
             sweep(cl)
         graphs.append(g)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % len(graphs)].replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    say(f"sweep: {ms * 1e3:.1f} us/step, {step_bytes / (ms * 1e-3) / 1e9:.1f} GB/s")
-
-    # per-launch kernel durations (eager, events bracketing each launch)
-    per = []
-    tot_b = 0
-    for rep in range(3):
-        for cl in calls:
-            for x, q, s, y in cl:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                aql.aql_linear_w8a16(x, q, s, None, y)
-                b.record()
-                per.append((a, b, nbytes(x, q, y)))
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b, _ in per]
-    tot_b = sum(nb for _, _, nb in per)
-    avg_ms = sum(durs) / len(durs)
-    achieved = tot_b / (sum(durs) * 1e-3) / 1e9
-    return ms, avg_ms, achieved, len(durs)
+    med, _ = event_time_ms(torch, lambda i: graphs[i].replay(), reps, len(graphs))
+    row = {"workload": "smolvlm500m_decode_sweep as 96 W8A16 launches in a HIP graph",
+           "us": med * 1e3, "GB/s": step_bytes / (med * 1e-3) / 1e9,
+           "frac_hbm": step_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    say(row)
+    return row
 
 
 # -------------------------------------------------------------- secondary
@@ -181,7 +183,7 @@ def sec_llm7b(torch, aql, workloads, dev):
             fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
             for i in range(ncopy):
                 fn(i)
-            med, _ = event_time_ms(torch, fn, 60, ncopy)
+            med, _ = event_time_ms(torch, fn, 50, ncopy)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N
             gbs = nb / (med * 1e-3) / 1e9
             rows.append({"workload": f"llm7b_w8a16 K={K} N={N} M={M}", "us": med * 1e3,
@@ -216,9 +218,9 @@ def sec_q8ta(torch, aql, workloads, dev):
                                                  two, s2, 0, y, wsb)
         for i in range(ncopy):
             fn(i)
-        med, _ = event_time_ms(torch, fn, 60, ncopy)
+        med, _ = event_time_ms(torch, fn, 40, ncopy)
         pro = lambda i: aql.aql_quantize_act_per_tensor(x, s1, z1, two, s2, 0, xq1, xq2)
-        pmed, _ = event_time_ms(torch, pro, 30, 1)
+        pmed, _ = event_time_ms(torch, pro, 40, 1)
         ops = (2 if two else 1) * 2 * M * N * K
         nb = 4 * M * K + N * K + 8 * N + 4 * M * N
         gemm_ms = max(med - pmed, 1e-6)
@@ -249,7 +251,7 @@ def sec_dq8ca(torch, aql, workloads, dev):
                                             None, y, workspace=wsb)
         for i in range(ncopy):
             fn(i)
-        med, _ = event_time_ms(torch, fn, 40, ncopy)
+        med, _ = event_time_ms(torch, fn, 20 if M > 1000 else 40, ncopy)
         ops = 2 * M * N * K
         nb = N * K // 2 + 4 * gs.numel() + 4 * M * K + 4 * M * N + 8 * M
         rows.append({"workload": f"dq8ca_8da4w M={M} K={K} N={N}", "us": med * 1e3,
@@ -328,16 +330,17 @@ def main():
     say(f"device: {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
 
     secondary = []
-    if args.only in (None, "sweep"):
-        calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
-        ms, avg_ms, achieved, nlaunch = run_sweep(torch, aql, dev, args, calls, step_bytes, nbytes)
-        del calls
-        torch.cuda.empty_cache()
     if args.only is not None and args.only != "sweep":
         fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
         return
-    if not args.no_secondary:
+    calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
+    ms = run_sweep(torch, aql, dev, args, calls, step_bytes)
+    if args.only is None and not args.no_secondary:
+        secondary.append(sweep_as_graph(torch, aql, calls, step_bytes))
+    del calls
+    torch.cuda.empty_cache()
+    if args.only is None and not args.no_secondary:
         for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant):
             secondary += fn(torch, aql, workloads, dev)
             torch.cuda.empty_cache()
@@ -364,21 +367,22 @@ def main():
         "config": {
             "workload": "smolvlm500m_decode_sweep: 32 layers x (up 2560x960, gate 2560x960, "
                         "down 960x2560) W8A16 GEMVs, M=1, bf16 x, int8 per-channel weights, "
-                        "3 rotated weight copies (712 MB)",
+                        "one grouped launch per sweep, 3 rotated weight copies (712 MB)",
             "gemvs_per_step": 96,
             "bytes_per_step": step_bytes,
             "frac_hbm": value / HBM_PEAK_GBS,
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": achieved,
+            "achieved": value,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
+            "frac": value / HBM_PEAK_GBS,
             "traffic": None,
-            "kernel": "k_w8a16_skinny",
-            "avg_launch_us": avg_ms * 1e3,
-            "launches_timed": nlaunch,
+            "kernel": "k_w8a16_grouped",
+            "bytes_per_launch": step_bytes,
+            "avg_launch_us": ms * 1e3,
+            "launches_timed": args.steps,
         },
         "cpu_baseline": cpu,
         "secondary": secondary,

@@ -242,6 +242,49 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
                      int64_t N, float *y, float *x_scale_out, int32_t *x_zp_out, void *ws,
                      size_t ws_bytes, void *stream);
 
+/* ----------------------------------------------------------- grouped W8A16 */
+
+/*
+ * Several independent W8A16 linears in one launch: the same operation as
+ * aql_linear_w8a16 on each problem, with all problems' tiles in one grid, so
+ * that a decode step's linears that do not feed one another (a sweep over the
+ * layers' MLP weights, or up and gate sharing x) stream their weights back to
+ * back instead of paying a launch and a pipeline fill per linear ([flashrt
+ * schemes] W8A16Decode: the decode band is bound by reading the weights).
+ *
+ * Plan / execute. aql_w8a16_group_plan validates the problems on the host and
+ * writes a table (aql_w8a16_group_table_bytes(count) bytes of host memory);
+ * the caller copies that table unchanged into device memory (any host-to-device
+ * copy) and launches with aql_linear_w8a16_grouped, passing the host table
+ * (read for the grid size) and its device copy (read by the kernel). The
+ * launch allocates and copies nothing, so it can be captured in a HIP graph.
+ * The table holds the problems' device pointers: it stays valid while they do.
+ */
+typedef struct aql_w8a16_problem {
+  const uint16_t *x;     /* device, [M, K] bf16 */
+  const int8_t *q;       /* device, [N, K] int8 */
+  const float *scale;    /* device, [N] float32 */
+  const uint16_t *bias;  /* device, [N] bf16, may be NULL */
+  uint16_t *y;           /* device, [M, N] bf16 (output) */
+  int64_t M, N, K;       /* as in aql_linear_w8a16; M or N == 0 skips the problem */
+} aql_w8a16_problem;
+
+/* Bytes of the table for `count` problems (0 if count < 1). */
+size_t aql_w8a16_group_table_bytes(int count);
+
+/* Validate `count` problems (each as aql_linear_w8a16 would) and write the
+ * table. Errors: count < 1, table NULL or smaller than
+ * aql_w8a16_group_table_bytes(count) (AQL_ERR_WORKSPACE), any problem invalid
+ * (its index is in aql_last_error()), more than 2^31 - 1 tiles in total. */
+int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *table,
+                         size_t table_bytes);
+
+/* Run a planned group. table: the host table written by aql_w8a16_group_plan;
+ * dev_table: its device copy (16-byte aligned). Errors: table not written by
+ * the plan function (AQL_ERR_PARAM), dev_table NULL or misaligned. A group
+ * whose problems are all empty returns AQL_OK without launching. */
+int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *stream);
+
 /* ------------------------------------------------------------ stage entry */
 
 /*

@@ -162,3 +162,41 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         aql.aql_gemm_i8_i32(torch.zeros(4, 64, dtype=torch.int8), torch.zeros(4, 64, dtype=torch.int8))
+
+
+def _problems(n, over=None):
+    over = over or {}
+    arr = (aql._Problem * n)()
+    for i in range(n):
+        d = dict(x=0x10000, q=0x20000, scale=0x30000, bias=0, y=0x40000, M=1, N=32, K=64)
+        d.update(over.get(i, {}))
+        arr[i] = aql._Problem(d["x"], d["q"], d["scale"], d["bias"], d["y"], d["M"], d["N"], d["K"])
+    return arr
+
+
+def test_group_plan_validation():
+    """The grouped W8A16 plan is host-only: it validates every problem and writes
+    the table without touching device memory."""
+    import numpy as np
+    nb = aql.aql_w8a16_group_table_bytes(3)
+    assert nb == 64 + 3 * 80 and aql.aql_w8a16_group_table_bytes(0) == 0
+    buf = np.zeros(nb, np.uint8)
+    tp = C.c_void_p(buf.ctypes.data)
+    f = L.aql_w8a16_group_plan
+    assert f(C.cast(_problems(3), C.c_void_p), 3, tp, nb) == aql.AQL_OK
+    hdr = buf[:20].view(np.int32)
+    assert hdr[2] == 3 and hdr[3] == 3 * 2  # 3 problems x 2 tiles of 16 channels
+    assert f(C.cast(_problems(3), C.c_void_p), 3, tp, nb - 1) == aql.AQL_ERR_WORKSPACE
+    assert f(C.cast(_problems(3), C.c_void_p), 0, tp, nb) == aql.AQL_ERR_SHAPE
+    assert f(C.cast(_problems(3, {1: dict(K=40)}), C.c_void_p), 3, tp, nb) == aql.AQL_ERR_SHAPE
+    assert "problem 1" in aql.aql_last_error()
+    assert f(C.cast(_problems(3, {2: dict(q=0)}), C.c_void_p), 3, tp, nb) == aql.AQL_ERR_NULL
+    assert f(C.cast(_problems(3, {0: dict(y=0x40004)}), C.c_void_p), 3, tp, nb) == aql.AQL_ERR_ALIGN
+    # empty problems are dropped from the table
+    assert f(C.cast(_problems(3, {1: dict(M=0, x=0, q=0, y=0)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
+    assert buf[:20].view(np.int32)[2] == 2
+    # a table not written by the plan is refused; an all-empty group is a no-op
+    bad = np.zeros(nb, np.uint8)
+    assert L.aql_linear_w8a16_grouped(C.c_void_p(bad.ctypes.data), A, None) == aql.AQL_ERR_PARAM
+    assert f(C.cast(_problems(1, {0: dict(N=0, q=0, scale=0, y=0)}), C.c_void_p), 1, tp, nb) == aql.AQL_OK
+    assert L.aql_linear_w8a16_grouped(tp, None, None) == aql.AQL_OK

@@ -353,3 +353,59 @@ def test_empty_problems_are_noops():
     s = torch.ones(8, dtype=torch.float32, device=DEV)
     y = aql.aql_linear_w8a16(x, q, s)
     assert tuple(y.shape) == (0, 8)
+
+
+def test_w8a16_grouped_mixed():
+    """One grouped launch over ragged problems (different M, N, K, with and
+    without bias, one empty) equals each problem's oracle result."""
+    g = workloads.gen(700)
+    shapes = [(1, 2560, 960, False), (1, 960, 2560, True), (4, 100, 80, False), (0, 64, 64, False),
+              (17, 33, 4112, True), (16, 1, 16, False), (1, 14336, 4096, False)]
+    probs, refs = [], []
+    for M, N, K, hb in shapes:
+        w = workloads.small_matrix(g, N, K, std=0.02)
+        x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+        b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16) if hb else None
+        q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        probs.append((dev(x), q, s, None if b is None else dev(b), y))
+        refs.append((x, b))
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    for rep in range(2):
+        for p in probs:
+            p[4].fill_(float("nan"))
+        aql.aql_linear_w8a16_grouped(host_t, dev_t)
+        for (x, q, s, b, y), (xc, bc) in zip(probs, refs):
+            if x.shape[0] == 0:
+                continue
+            yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s),
+                                            None if bc is None else bits(bc))
+            check_float(host(y.float()), yref, tol, BF16, f"grouped {tuple(y.shape)}")
+
+
+def test_w8a16_grouped_smolvlm_sweep_in_graph():
+    """The decode sweep as one grouped launch, captured in a HIP graph and
+    replayed three times, each replay checked against the oracle."""
+    layers = workloads.smolvlm(seed=1, layers=8)
+    probs, refs = [], []
+    for L in layers:
+        for wn, xn in (("w_up", "x_up"), ("w_gate", "x_up"), ("w_down", "x_down")):
+            q, s, _ = aql.aql_quantize_weight_int8(dev(L[wn]), aql.AQL_WQ_SYM127)
+            x = dev(L[xn])
+            y = torch.empty(1, q.shape[0], dtype=torch.bfloat16, device=DEV)
+            probs.append((x, q, s, None, y))
+            refs.append(L[xn])
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        aql.aql_linear_w8a16_grouped(host_t, dev_t)
+    expect = [oracle.linear_w8a16(bits(xc), host(p[1]), host(p[2])) for p, xc in zip(probs, refs)]
+    for rep in range(3):
+        for p in probs:
+            p[4].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, (yref, tol) in zip(probs, expect):
+            check_float(host(p[4].float()), yref, tol, BF16, f"graph replay {rep}")

@@ -94,7 +94,9 @@ struct GroupHeader {
   int32_t count;         // entries that follow (non-empty problems)
   int32_t total_blocks;  // grid size
   int32_t waves;         // waves per workgroup
-  int32_t reserved[11];
+  int32_t mblocks;       // 4-row blocks of x per tile
+  int32_t tgroups;       // 4-channel groups per tile
+  int32_t reserved[9];
 };
 static_assert(sizeof(GroupHeader) == 64, "table header");
 constexpr uint32_t kGroupMagic = 0x47514c41u;  // "ALQG"
@@ -227,15 +229,27 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
           "%s: table needs %zu bytes", fn, aql_w8a16_group_table_bytes(count));
   GroupHeader *h = static_cast<GroupHeader *>(table);
   aql::W8A16GroupEntry *e = reinterpret_cast<aql::W8A16GroupEntry *>(h + 1);
-  int64_t blocks = 0, kmin = 0;
-  int n = 0;
+  // One launch shape for the whole group, from the smallest K and the largest M.
+  int64_t kmin = 0, mmax = 0, nsum = 0;
   for (int i = 0; i < count; ++i) {
     const aql_w8a16_problem &p = problems[i];
     char name[64];
     snprintf(name, sizeof name, "%s: problem %d", fn, i);
     if (int rc = check_w8a16(name, p.x, p.M, p.K, p.q, p.scale, p.bias, p.N, p.y)) return rc;
     if (p.M == 0 || p.N == 0) continue;
-    const int64_t nblk = (p.N + 15) / 16, mblk = (p.M + 15) / 16;
+    kmin = (kmin == 0 || p.K < kmin) ? p.K : kmin;
+    mmax = p.M > mmax ? p.M : mmax;
+    nsum += p.N * ((p.M + 15) / 16);
+  }
+  aql::W8A16Shape sh = aql::w8a16_shape(mmax ? mmax : 1, nsum ? nsum : 1, kmin ? kmin : 16);
+  if (sh.waves > 8) sh.waves = 8;
+  const int64_t rows = 4 * sh.tgroups;
+  int64_t blocks = 0;
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    const aql_w8a16_problem &p = problems[i];
+    if (p.M == 0 || p.N == 0) continue;
+    const int64_t nblk = (p.N + rows - 1) / rows, mblk = (p.M + 15) / 16;
     REQUIRE(blocks + nblk * mblk <= 0x7fffffffLL, AQL_ERR_SHAPE, "%s: too many tiles in total",
             fn);
     aql::W8A16GroupEntry &d = e[n++];
@@ -251,15 +265,15 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
     d.blk_begin = (int32_t)blocks;
     d.nblk = (int32_t)nblk;
     blocks += nblk * mblk;
-    kmin = (kmin == 0 || p.K < kmin) ? p.K : kmin;
   }
   *h = GroupHeader{};
   h->magic = kGroupMagic;
   h->version = 1;
   h->count = n;
   h->total_blocks = (int32_t)blocks;
-  int w = n ? aql::w8a16_waves(kmin, blocks) : 1;
-  h->waves = w > 8 ? 8 : w;
+  h->waves = sh.waves;
+  h->mblocks = sh.mblocks;
+  h->tgroups = sh.tgroups;
   return ok();
 }
 
@@ -268,7 +282,9 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   REQUIRE(table, AQL_ERR_NULL, "%s: table must not be NULL", fn);
   const GroupHeader *h = static_cast<const GroupHeader *>(table);
   REQUIRE(h->magic == kGroupMagic && h->version == 1 && h->count >= 0 && h->total_blocks >= 0 &&
-              (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8),
+              (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8) &&
+              (h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4) &&
+              (h->tgroups == 1 || h->tgroups == 2 || h->tgroups == 4),
           AQL_ERR_PARAM, "%s: table was not written by aql_w8a16_group_plan", fn);
   if (h->count == 0 || h->total_blocks == 0) return ok();
   REQUIRE(dev_table, AQL_ERR_NULL, "%s: dev_table must not be NULL", fn);
@@ -276,7 +292,11 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   if (int e = check_device(fn)) return e;
   const aql::W8A16GroupEntry *dev_entries = reinterpret_cast<const aql::W8A16GroupEntry *>(
       static_cast<const char *>(dev_table) + sizeof(GroupHeader));
-  return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, h->waves,
+  aql::W8A16Shape sh;
+  sh.waves = h->waves;
+  sh.mblocks = h->mblocks;
+  sh.tgroups = h->tgroups;
+  return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, sh,
                                             (hipStream_t)stream),
                   fn);
 }

@@ -42,8 +42,15 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st);
 
-// Waves per workgroup the W8A16 kernel uses for K and a grid of `blocks` tiles.
-int w8a16_waves(int64_t K, int64_t blocks);
+// Launch shape of the W8A16 kernel: waves per workgroup, groups of 4 output
+// channels per tile (1, 2 or 4) and blocks of 4 rows of x per tile (1, 2 or 4).
+struct W8A16Shape {
+  int waves, tgroups, mblocks;
+};
+W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K);
+hipError_t launch_w8a16_shape(const W8A16Shape &sh, const uint16_t *x, int64_t M, int64_t K,
+                              const int8_t *q, const float *scale, const uint16_t *bias,
+                              int64_t N, uint16_t *y, hipStream_t st);
 
 // One problem of a grouped W8A16 launch, as stored in the device table.
 struct W8A16GroupEntry {
@@ -54,13 +61,13 @@ struct W8A16GroupEntry {
   uint16_t *y;
   int64_t M, N, K;
   int32_t blk_begin;  // first grid block of this problem
-  int32_t nblk;       // 16-channel blocks along N
+  int32_t nblk;       // tiles along N
   int32_t pad[2];
 };
 static_assert(sizeof(W8A16GroupEntry) == 80, "table layout");
 
 hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
-                                int waves, hipStream_t st);
+                                const W8A16Shape &sh, hipStream_t st);
 
 // int8 GEMM epilogues
 enum GemmEpi { EPI_RAW = 0, EPI_Q8TA = 1, EPI_DQ8 = 2 };

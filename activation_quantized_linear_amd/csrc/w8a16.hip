@@ -4,15 +4,23 @@
 // int8 -> bf16 is exact, so the sum can run on the bf16 matrix cores with the
 // int8 codes widened in registers and the scale applied once per output.
 //
-// Tile: one workgroup owns 16 output channels and 16 rows of x; its W waves
-// split K into 64-wide chunks (wave w takes chunks w, w + W, ...). Per chunk a
-// lane reads 16 int8 weights of one channel (a wave covers 16 channels x 64
-// contiguous bytes) and the matching 16 bf16 of x, widens the weights and
-// issues two v_mfma_f32_16x16x32_bf16; the MFMA does the K reduction across
-// the lanes. Loads are buffer loads: the hardware range check returns zero
-// past the end of the tile's rows (no branches, 32-bit offsets), and chunks
-// are fetched in batches of U with the next batch in flight while the current
-// one is multiplied. The waves' partial 16x16 tiles meet once in LDS.
+// Access shape. The kernel is bound by streaming the weights from HBM. On
+// gfx950 a wave instruction that reads 4 rows x 256 contiguous bytes streams
+// markedly faster than the 16 rows x 64 bytes a 16x16 MFMA fragment would ask
+// for, so the weights are loaded in that 4-row shape and multiplied where they
+// land with v_mfma_f32_4x4x4_16b_bf16: its 16 blocks of 4 lanes each take one
+// 16-byte k-slice (block b = lane / 4) of 4 weight rows (column j = lane % 4),
+// against the same k-slice of 4 rows of x (row i = lane % 4 of the A operand).
+//
+// Tile: one workgroup owns 16 output channels (4 row groups t of 4) and up to
+// 16 rows of x (MB blocks of 4); its W waves split K into 256-byte steps (wave
+// w takes steps w, w + W, ...). Per step a lane loads 16 weight bytes of each
+// row group and the 16 matching bf16 of x per m block, and issues 4 MFMAs per
+// (t, m block). Loads are buffer loads: the hardware range check returns zero
+// past the tile's rows and past K (no branches), and steps are fetched in
+// batches of U with the next batch in flight while the current one is
+// multiplied. At the end the 16 k-slice partials are summed across lanes
+// (shuffles over lane bits 2..5) and the waves' tiles meet once in LDS.
 //
 // Launches: a single problem (grid = N/16 x M/16 tiles), or a group of
 // independent problems in one launch (a decode sweep's linears), whose tiles
@@ -21,6 +29,8 @@
 
 namespace aql {
 namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int OOB = 0x40000000;  // an offset past any tile's range: loads return 0
 
@@ -37,14 +47,11 @@ __device__ __forceinline__ uint32_t bf16x2_from_i8(int lo, int hi) {
                                0x07060302u);
 }
 
-// 8 int8 codes (two dwords, little-endian) -> 8 bf16 in order.
-__device__ __forceinline__ bf16x8 widen8(int w0, int w1) {
-  i32x4 r;
-  r.x = (int)bf16x2_from_i8((int)(int8_t)(w0), (int)(int8_t)(w0 >> 8));
-  r.y = (int)bf16x2_from_i8((int)(int8_t)(w0 >> 16), (w0 >> 24));
-  r.z = (int)bf16x2_from_i8((int)(int8_t)(w1), (int)(int8_t)(w1 >> 8));
-  r.w = (int)bf16x2_from_i8((int)(int8_t)(w1 >> 16), (w1 >> 24));
-  return __builtin_bit_cast(bf16x8, r);
+// Four int8 codes (one dword, little-endian) -> four bf16 in order.
+__device__ __forceinline__ s16x4 widen4(int w) {
+  const uint32_t lo = bf16x2_from_i8((int)(int8_t)(w), (int)(int8_t)(w >> 8));
+  const uint32_t hi = bf16x2_from_i8((int)(int8_t)(w >> 16), (w >> 24));
+  return __builtin_bit_cast(s16x4, (uint64_t)lo | ((uint64_t)hi << 32));
 }
 
 struct Tile {
@@ -57,92 +64,158 @@ struct Tile {
   int64_t n0, m0;
 };
 
-template <int W, int U>
-__device__ __forceinline__ void w8a16_tile(const Tile &t, f32x4 (*red)[64]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
+// LDS for the cross-wave reduction: per wave, per (row group, m block), per
+// column j, four rows of x.
+template <int W, int TG, int MB>
+struct Red {
+  f32x4 v[W][TG][MB][4];
+};
+
+// TG row groups of 4 output channels per tile (4 TG channels), MB blocks of 4
+// rows of x, W waves, U steps per fetched batch.
+template <int W, int TG, int MB, int U>
+__device__ __forceinline__ void w8a16_tile(const Tile &t, Red<W, TG, MB> &red) {
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar) so that per-step offsets are scalar selects, not branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, blk = lane >> 2;  // column (weight row in group) / k-slice
   const int64_t K = t.K;
-  const int64_t nrows = t.N - t.n0 < 16 ? t.N - t.n0 : 16;
+  const int64_t nrows = t.N - t.n0 < 4 * TG ? t.N - t.n0 : 4 * TG;
   const int64_t mrows = t.M - t.m0 < 16 ? t.M - t.m0 : 16;
   const __amdgpu_buffer_rsrc_t rq = rsrc(t.q + t.n0 * K, (uint32_t)(nrows * K));
   const __amdgpu_buffer_rsrc_t rx = rsrc(t.x + t.m0 * K, (uint32_t)(mrows * K * 2));
-  const uint32_t qlane = (uint32_t)(r * K + g * 16);
-  const uint32_t xlane = 2u * qlane;
-  const int nch = (int)((K + 63) >> 6);
-  const int cnt = wave < nch ? (nch - wave + W - 1) / W : 0;
+  // weights: row group tg, lane -> row 4 tg + j, bytes 16 blk of the step
+  const uint32_t qlane = (uint32_t)(j * K + 16 * blk);
+  // x: m block mb, lane -> row 4 mb + j of x (the A operand row is lane % 4)
+  const uint32_t xlane = 2u * (uint32_t)(j * K + 16 * blk);
+  const int nst = (int)((K + 255) >> 8);
+  const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
 
-  i32x4 wv[U], xa[U], xb[U];
-  auto fetch = [&](int i0, i32x4 *w_, i32x4 *a_, i32x4 *b_) {
+  f32x4 acc[TG][MB];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[tg][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one step: 4 weight loads (row groups), 2 x loads per m block
+  auto fetch = [&](int i0, i32x4 (*w_)[TG], i32x4 (*x_)[MB][2]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
-      const int c = wave + W * i;
-      const bool valid = i < cnt;
-      const bool kin = valid && (64 * c + 16 * g) < K;
-      const int qo = valid ? (int)(qlane + 64u * c) : OOB;
-      const int xo = kin ? (int)(xlane + 128u * c) : OOB;
-      w_[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
-      a_[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
-      b_[u] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, 0, 0);
+      const int st = wave + W * i;
+      const bool valid = i < cnt;  // uniform
+      // per-lane: this lane's 16-byte k-slice lies before K (only the last step can end early)
+      const bool kin = (256 * st + 16 * blk) < K;
+      const uint32_t qstep = valid ? 256u * st : (uint32_t)OOB;
+      const uint32_t xstep = valid ? 512u * st : (uint32_t)OOB;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        const int qo = (int)(qlane + (uint32_t)(4 * tg) * (uint32_t)K + qstep);
+        w_[u][tg] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int xo = kin ? (int)(xlane + 2u * (uint32_t)(4 * mb) * (uint32_t)K + xstep) : OOB;
+        x_[u][mb][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+        x_[u][mb][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, 0, 0);
+      }
     }
   };
+  auto mul = [&](i32x4 (*w_)[TG], i32x4 (*x_)[MB][2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const s16x4 b = widen4(w_[u][tg][e]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const i32x4 xv = x_[u][mb][e >> 1];
+            const s16x4 a = __builtin_bit_cast(
+                s16x4, (uint64_t)(uint32_t)xv[(e & 1) * 2] |
+                           ((uint64_t)(uint32_t)xv[(e & 1) * 2 + 1] << 32));
+            acc[tg][mb] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, acc[tg][mb], 0, 0, 0);
+          }
+        }
+  };
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  fetch(0, wv, xa, xb);
-  for (int b = 0; b < cnt; b += U) {
-    i32x4 wn[U], xan[U], xbn[U];
-    fetch(b + U, wn, xan, xbn);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u]),
-                                                    widen8(wv[u].x, wv[u].y), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xb[u]),
-                                                    widen8(wv[u].z, wv[u].w), acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wv[u] = wn[u];
-      xa[u] = xan[u];
-      xb[u] = xbn[u];
-    }
+  // Ping-pong over two register batches; sched_barrier keeps the compiler from
+  // regrouping the phases, and a batch past the wave's last step loads zeros
+  // so the loop needs no early exit (one would let the loads sink).
+  i32x4 w0[U][TG], w1[U][TG], x0[U][MB][2], x1[U][MB][2];
+  fetch(0, w0, x0);
+  for (int b = 0; b < cnt; b += 2 * U) {
+    fetch(b + U, w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(b + 2 * U, w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  if constexpr (W > 1) {
-    if (wave > 0) red[wave - 1][lane] = acc;
-    __syncthreads();
-    if (wave != 0) return;
+  // Sum the 16 k-slice blocks: lanes j, j + 4, ..., j + 60.
 #pragma unroll
-    for (int i = 0; i < W - 1; ++i) acc += red[i][lane];
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[tg][mb][v] += __shfl_xor(acc[tg][mb][v], o);
+
+  if (lane < 4) {
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red.v[wave][tg][mb][j] = acc[tg][mb];
   }
-  // lane holds D[4g + v][r]: row m0 + 4g + v of x, output channel n0 + r.
-  const int64_t n = t.n0 + r;
+  if constexpr (W > 1) __syncthreads();
+  // wave 0, lanes 0..4TG-1: output channel n0 + lane (row group lane / 4, column lane % 4)
+  if (wave != 0 || lane >= 4 * TG) return;
+  const int tg = lane >> 2, jj = lane & 3;
+  const int64_t n = t.n0 + lane;
   if (n >= t.N) return;
   const float s = t.scale[n];
   const float bv = t.bias ? bf16_to_f32(t.bias[n]) : 0.0f;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t mm = t.m0 + 4 * g + v;
-    if (mm < t.M) t.y[mm * t.N + n] = f32_to_bf16_rne(s * acc[v] + bv);
+  for (int mb = 0; mb < MB; ++mb) {
+    f32x4 sum = red.v[0][tg][mb][jj];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red.v[w][tg][mb][jj];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mm = t.m0 + 4 * mb + v;
+      if (mm < t.M) t.y[mm * t.N + n] = f32_to_bf16_rne(s * sum[v] + bv);
+    }
   }
 }
 
-template <int W, int U>
+template <int TG, int MB>
+constexpr int batch_steps() {
+  return TG * MB <= 8 ? 2 : 1;
+}
+
+template <int W, int TG, int MB>
 __global__ __launch_bounds__(64 * W) void k_w8a16(const uint16_t *__restrict__ x, int64_t M,
                                                   int64_t K, const int8_t *__restrict__ q,
                                                   const float *__restrict__ scale,
                                                   const uint16_t *__restrict__ bias, int64_t N,
                                                   uint16_t *__restrict__ y) {
-  __shared__ f32x4 red[W > 1 ? W - 1 : 1][64];
-  const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 16, (int64_t)blockIdx.y * 16};
-  w8a16_tile<W, U>(t, red);
+  __shared__ Red<W, TG, MB> red;
+  const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 4 * TG,
+               (int64_t)blockIdx.y * 16};
+  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
 }
 
 // Grouped launch: blocks [begin, begin + nblk * mblk) of the grid belong to
 // problem p, n-block fastest. The table is read through the scalar cache.
-template <int W, int U>
+template <int W, int TG, int MB>
 __global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry *__restrict__ tab,
                                                           int count) {
-  __shared__ f32x4 red[W > 1 ? W - 1 : 1][64];
+  __shared__ Red<W, TG, MB> red;
   const int blk = blockIdx.x;
   int lo = 0, hi = count - 1;
   while (lo < hi) {  // last entry with begin <= blk
@@ -153,56 +226,103 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry 
   const W8A16GroupEntry &e = tab[lo];
   const int local = blk - e.blk_begin;
   const int nb = local % e.nblk, mb = local / e.nblk;
-  const Tile t{e.x, e.q, e.scale, e.bias, e.y, e.M, e.N, e.K, (int64_t)nb * 16, (int64_t)mb * 16};
-  w8a16_tile<W, U>(t, red);
+  const Tile t{e.x, e.q, e.scale, e.bias, e.y, e.M, e.N, e.K, (int64_t)nb * 4 * TG,
+               (int64_t)mb * 16};
+  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
 }
 
-template <int W>
-void launch_w(dim3 grid, hipStream_t st, const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
-              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y) {
-  hipLaunchKernelGGL((k_w8a16<W, 4>), grid, dim3(64 * W), 0, st, x, M, K, q, scale, bias, N, y);
+template <int TG, int MB>
+void launch_single(int W, dim3 grid, hipStream_t st, const uint16_t *x, int64_t M, int64_t K,
+                   const int8_t *q, const float *scale, const uint16_t *bias, int64_t N,
+                   uint16_t *y) {
+  switch (W) {
+#define AQL_W(w)                                                                              \
+  case w:                                                                                     \
+    hipLaunchKernelGGL((k_w8a16<w, TG, MB>), grid, dim3(64 * w), 0, st, x, M, K, q, scale, bias, \
+                       N, y);                                                                 \
+    break;
+    AQL_W(16) AQL_W(8) AQL_W(4) AQL_W(2) default : AQL_W(1)
+#undef AQL_W
+  }
 }
 
-template <int W>
-void launch_g(int blocks, hipStream_t st, const W8A16GroupEntry *tab, int count) {
-  hipLaunchKernelGGL((k_w8a16_grouped<W, 4>), dim3((unsigned)blocks), dim3(64 * W), 0, st, tab,
-                     count);
+template <int TG, int MB>
+void launch_group(int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab, int count) {
+  const dim3 grid((unsigned)blocks);
+  switch (W) {
+#define AQL_W(w)                                                                            \
+  case w:                                                                                   \
+    hipLaunchKernelGGL((k_w8a16_grouped<w, TG, MB>), grid, dim3(64 * w), 0, st, tab, count); \
+    break;
+    AQL_W(16) AQL_W(8) AQL_W(4) AQL_W(2) default : AQL_W(1)
+#undef AQL_W
+  }
+}
+
+template <int TG>
+void launch_single_tg(int MB, int W, dim3 grid, hipStream_t st, const uint16_t *x, int64_t M,
+                      int64_t K, const int8_t *q, const float *scale, const uint16_t *bias,
+                      int64_t N, uint16_t *y) {
+  switch (MB) {
+    case 1: launch_single<TG, 1>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
+    case 2: launch_single<TG, 2>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
+    default: launch_single<TG, 4>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
+  }
+}
+
+template <int TG>
+void launch_group_tg(int MB, int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab,
+                     int count) {
+  switch (MB) {
+    case 1: launch_group<TG, 1>(W, blocks, st, tab, count); break;
+    case 2: launch_group<TG, 2>(W, blocks, st, tab, count); break;
+    default: launch_group<TG, 4>(W, blocks, st, tab, count); break;
+  }
 }
 
 }  // namespace
 
-int w8a16_waves(int64_t K, int64_t blocks) {
-  const int64_t nch = (K + 63) / 64;
-  int W = 4;
-  if (blocks < 256) W = 16;
-  else if (blocks < 512) W = 8;
-  while (W > 1 && W * 2 > nch) W >>= 1;
-  return W;
+// Launch shape, from a sweep of tile rows x waves on the 7B MLP shapes and the
+// SmolVLM decode sweep: streaming is fastest with few waves per workgroup (no
+// cross-wave reduction) and on the order of a thousand or more wave-tiles in
+// flight; 8-channel tiles suit M <= 2, 16-channel tiles larger M.
+W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
+  W8A16Shape s;
+  s.mblocks = M <= 4 ? 1 : (M <= 8 ? 2 : 4);
+  s.tgroups = M <= 2 ? 2 : 4;
+  const int64_t nst = (K + 255) / 256;  // 256-byte K steps
+  const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
+  int W = 1;
+  while (W < 16 && tiles * W < 768 && W * 4 <= nst) W <<= 1;
+  s.waves = W;
+  return s;
+}
+
+hipError_t launch_w8a16_shape(const W8A16Shape &sh, const uint16_t *x, int64_t M, int64_t K,
+                              const int8_t *q, const float *scale, const uint16_t *bias,
+                              int64_t N, uint16_t *y, hipStream_t st) {
+  const int64_t rows = 4 * sh.tgroups;
+  const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)((M + 15) / 16));
+  switch (sh.tgroups) {
+    case 1: launch_single_tg<1>(sh.mblocks, sh.waves, grid, st, x, M, K, q, scale, bias, N, y); break;
+    case 2: launch_single_tg<2>(sh.mblocks, sh.waves, grid, st, x, M, K, q, scale, bias, N, y); break;
+    default: launch_single_tg<4>(sh.mblocks, sh.waves, grid, st, x, M, K, q, scale, bias, N, y); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st) {
-  const int64_t nblk = (N + 15) / 16, mblk = (M + 15) / 16;
-  const int W = w8a16_waves(K, nblk * mblk);
-  const dim3 grid((unsigned)nblk, (unsigned)mblk);
-  switch (W) {
-    case 16: launch_w<16>(grid, st, x, M, K, q, scale, bias, N, y); break;
-    case 8: launch_w<8>(grid, st, x, M, K, q, scale, bias, N, y); break;
-    case 4: launch_w<4>(grid, st, x, M, K, q, scale, bias, N, y); break;
-    case 2: launch_w<2>(grid, st, x, M, K, q, scale, bias, N, y); break;
-    default: launch_w<1>(grid, st, x, M, K, q, scale, bias, N, y); break;
-  }
-  return hipGetLastError();
+  return launch_w8a16_shape(w8a16_shape(M, N, K), x, M, K, q, scale, bias, N, y, st);
 }
 
 hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
-                                int waves, hipStream_t st) {
-  switch (waves) {
-    case 8: launch_g<8>(total_blocks, st, dev_tab, count); break;
-    case 4: launch_g<4>(total_blocks, st, dev_tab, count); break;
-    case 2: launch_g<2>(total_blocks, st, dev_tab, count); break;
-    default: launch_g<1>(total_blocks, st, dev_tab, count); break;
+                                const W8A16Shape &sh, hipStream_t st) {
+  switch (sh.tgroups) {
+    case 1: launch_group_tg<1>(sh.mblocks, sh.waves, total_blocks, st, dev_tab, count); break;
+    case 2: launch_group_tg<2>(sh.mblocks, sh.waves, total_blocks, st, dev_tab, count); break;
+    default: launch_group_tg<4>(sh.mblocks, sh.waves, total_blocks, st, dev_tab, count); break;
   }
   return hipGetLastError();
 }

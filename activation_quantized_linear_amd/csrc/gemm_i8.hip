@@ -11,27 +11,38 @@
 // The zero points fold through the weight sums in exact int32 before any float
 // op, so the integer part is bit-exact whatever the tiling.
 //
-// Tiling: a 512-thread workgroup computes a 128 (A rows) x 128
-// (N) tile. Its 8 waves are 2 x 2 output quadrants of 64 x 64 (4 x 4 MFMA
-// tiles each) times 2 halves of every 128-byte K stage, so two waves share
-// each SIMD and one multiplies while the other waits on LDS; the halves' int32
-// accumulators are added once at the end. Operand tiles go from global memory
-// straight into a 4-stage LDS ring with buffer loads that write LDS (no
-// registers on the way, and the hardware range check zero-fills rows past M
-// or N and bytes past K). In LDS every 128-byte row stores its 16-byte chunks
-// XOR-swizzled by (row / 2) mod 8, so the 16 rows x 16 bytes an MFMA fragment
-// read touches hit distinct banks. Workgroups are mapped to tiles so that each
-// XCD (blocks are dealt to the 8 XCDs round-robin) works on a contiguous band
-// of N tiles, sharing them in its L2.
+// Tiling: a 512-thread workgroup computes a 128 (A rows) x 128 (N) tile. Its
+// 8 waves are 2 x 2 output quadrants of 64 x 64 (4 x 4 MFMA tiles each) times
+// 2 halves of every 128-byte K stage, so two waves share each SIMD; the halves'
+// int32 accumulators are added once at the end.
+//
+// Operand path: global memory -> LDS by buffer loads that write LDS directly
+// (no registers on the way; the hardware range check zero-fills rows past M or
+// N and bytes past K) into a 4-stage ring, three stages in flight. Every wave
+// waits for its own loads of the stage it is about to read (an explicit vmcnt
+// whose count the straight-line loop makes exact) and then meets the others at
+// a bare s_barrier: no memory fence, so loads of later stages stay in flight
+// across it. In LDS each 128-byte row stores its 16-byte chunks XOR-swizzled by
+// (row / 2) mod 8, so the 16 rows x 16 bytes a fragment read touches hit
+// distinct banks. Workgroups are mapped to tiles so that each XCD (blocks are
+// dealt to the 8 XCDs round-robin) works on a contiguous band of N tiles.
+//
+// Epilogue: the output tile is assembled in LDS (row stride 132 words, bank-
+// conflict free for the MFMA output layout) and written with 16-byte stores of
+// whole rows.
 #include "common.h"
 
 namespace aql {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 128, STAGES = 4;
-constexpr int ROWB = BK;                       // bytes per LDS row
+constexpr int ROWB = BK;                       // bytes per LDS ring row
 constexpr int STAGE_BYTES = (BM + BN) * ROWB;  // 32 KB
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+constexpr int XCH_BYTES = 4 * 16 * 64 * 16;    // 4 waves x 16 MFMA tiles x 64 lanes x 16 B
+constexpr int TILE_LD = BN + 4;                // words per staged output row
+constexpr int TILE_BYTES = BM * TILE_LD * 4;
+constexpr int LDS_BYTES = RING_BYTES > XCH_BYTES + TILE_BYTES ? RING_BYTES : XCH_BYTES + TILE_BYTES;
 constexpr int OOB = 0x40000000;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -43,15 +54,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// s_waitcnt with vmcnt = n (expcnt / lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0xF70); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0xF74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0xF78); break;
-    default: __builtin_amdgcn_s_waitcnt(0xF70); break;
-  }
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (N < 16).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
+// s_waitcnt lgkmcnt(0) (vmcnt / expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int EPI, bool TWO>
 __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int tiles_n) {
@@ -62,8 +72,9 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
   int tile = lin;
   if ((nt & 7) == 0) tile = (lin & 7) * (nt >> 3) + (lin >> 3);
   const int tn = tile / tiles_m, tm = tile % tiles_m;
+  constexpr int MROWS = TWO ? BM / 2 : BM;  // output rows per tile
   const int64_t n0 = (int64_t)tn * BN;
-  const int64_t m0 = (int64_t)tm * (TWO ? BM / 2 : BM);
+  const int64_t m0 = (int64_t)tm * MROWS;
   const int64_t M = p.M, N = p.N, K = p.K;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -71,55 +82,57 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
   const int kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
   const int r = lane & 15, g = lane >> 4;
 
-  // ---- loads: per stage 32 instructions of 8 rows x 128 B (16 A, 16 B); wave
-  // w issues A groups 2w, 2w+1 and B groups 2w, 2w+1. Lane i of a group loads
-  // row 8 * grp + i / 8 into LDS slot i % 8, i.e. global chunk (i % 8) ^ swz(row).
-  const int mrows = TWO ? BM / 2 : BM;
-  const int64_t mval = M - m0 < mrows ? M - m0 : mrows;
+  // ---- loads: per stage 32 instructions of 8 rows x 128 B. Wave w fills tile
+  // rows 16w .. 16w+15 of A and of B (2 instructions each). Lane i of an
+  // instruction writes LDS row 8q + i/8, slot i % 8, i.e. global chunk
+  // (i % 8) ^ swz(row). For the two-pass tile, rows [64h, 64h+32) hold pass-1
+  // rows 32h .. 32h+31 and rows [64h+32, 64h+64) the same rows of pass 2; a
+  // wave's 16 rows never straddle the halves, so its source is uniform.
+  const int64_t mval = M - m0 < MROWS ? M - m0 : MROWS;
   const int64_t nval = N - n0 < BN ? N - n0 : BN;
-  const __amdgpu_buffer_rsrc_t ra1 = rsrc(p.a1 + m0 * K, (uint32_t)(mval * K));
-  const __amdgpu_buffer_rsrc_t ra2 = rsrc(TWO ? p.a2 + m0 * K : p.a1, (uint32_t)(TWO ? mval * K : 0));
+  const bool apass2 = TWO && ((16 * wave) & 63) >= 32;
+  const int8_t *abase = apass2 ? p.a2 : p.a1;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(abase + m0 * K, (uint32_t)(mval * K));
   const __amdgpu_buffer_rsrc_t rb = rsrc(p.b + n0 * K, (uint32_t)(nval * K));
   uint32_t aoff[2], boff[2];
-  int achunk[2], bchunk[2];
-  bool apass2[2];
+  int chunk[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    const int grp = 2 * wave + q;
-    const int grow = 8 * grp;                 // first tile row of the group (uniform)
-    const int row = grow + (lane >> 3);       // tile row 0..127
-    const int c = (lane & 7) ^ swz(row);      // global chunk landing in slot lane % 8
-    int arow;  // row within its source buffer's tile
-    if constexpr (TWO) {
-      apass2[q] = (grow & 63) >= 32;          // 8-row groups never straddle a 32-row half
-      arow = 32 * (grow >> 6) + (row & 31);
-    } else {
-      apass2[q] = false;
-      arow = row;
-    }
+    const int row = 16 * wave + 8 * q + (lane >> 3);  // tile row 0..127
+    const int c = (lane & 7) ^ swz(row);
+    const int arow = TWO ? 32 * (row >> 6) + (row & 31) : row;
     aoff[q] = (uint32_t)arow * (uint32_t)K + 16u * c;
     boff[q] = (uint32_t)row * (uint32_t)K + 16u * c;
-    achunk[q] = 16 * c;
-    bchunk[q] = 16 * c;
+    chunk[q] = 16 * c;
   }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   auto issue = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * BK;
-    char *st = smem + (kt % STAGES) * STAGE_BYTES;
+    const uint32_t k0 = (uint32_t)kt * BK;
+    const uint32_t sa = lds_base + (uint32_t)((kt % STAGES) * STAGE_BYTES) + (uint32_t)(wave * 16 * ROWB);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const int grp = 2 * wave + q;
-      const bool kin = k0 + achunk[q] < K;
-      const int ao = kin ? (int)(aoff[q] + (uint32_t)k0) : OOB;
-      const int bo = (k0 + bchunk[q] < K) ? (int)(boff[q] + (uint32_t)k0) : OOB;
-      lds_void *da = (lds_void *)(st + grp * 8 * ROWB);
-      lds_void *db = (lds_void *)(st + BM * ROWB + grp * 8 * ROWB);
-      if (TWO && apass2[q])
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra2, da, 16, ao, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra1, da, 16, ao, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, db, 16, bo, 0, 0, 0);
+      const bool kin = (int64_t)k0 + chunk[q] < K;
+      const int ao = kin ? (int)(aoff[q] + k0) : OOB;
+      const int bo = kin ? (int)(boff[q] + k0) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(sa + q * 8 * ROWB), 16, ao, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(sa + BM * ROWB + q * 8 * ROWB), 16,
+          bo, 0, 0, 0);
     }
   };
+
+  // fragment offsets within a stage: 16 rows x this lane's 16-byte chunk
+  int fao[4], fbo[4];
+  {
+    const int c = 4 * kh + g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ra_ = wm * 64 + i * 16 + r, rb_ = wn * 64 + i * 16 + r;
+      fao[i] = ra_ * ROWB + 16 * (c ^ swz(ra_));
+      fbo[i] = BM * ROWB + rb_ * ROWB + 16 * (c ^ swz(rb_));
+    }
+  }
 
   i32x4 acc[4][4];
 #pragma unroll
@@ -127,37 +140,52 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
 
-  const int nk = (int)((K + BK - 1) / BK);
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt's loads are this wave's oldest; the ones issued after it may stay
-    const int ahead = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
-    wait_vm(4 * ahead);
-    __syncthreads();  // every wave's part of stage kt is in LDS; slot kt-1 is free
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-
+  auto compute = [&](int kt) {
     const char *st = smem + (kt % STAGES) * STAGE_BYTES;
-    const int c = 4 * kh + g;  // this lane's 16-byte chunk in the stage
     i32x4 fa[4], fb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ra_ = wm * 64 + i * 16 + r;
-      const int rb_ = wn * 64 + i * 16 + r;
-      fa[i] = *reinterpret_cast<const i32x4 *>(st + ra_ * ROWB + 16 * (c ^ swz(ra_)));
-      fb[i] = *reinterpret_cast<const i32x4 *>(st + BM * ROWB + rb_ * ROWB + 16 * (c ^ swz(rb_)));
+      fa[i] = *reinterpret_cast<const i32x4 *>(st + fao[i]);
+      fb[i] = *reinterpret_cast<const i32x4 *>(st + fbo[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Prologue issues stages 0 .. STAGES-2 (ranges past K load zeros). The main
+  // loop keeps STAGES-1 stages in flight; the tail drains them. Every wave
+  // issues 4 loads per stage, so "stage kt landed" is vmcnt <= 4 x (stages
+  // issued after it).
+  const int nk = (int)((K + BK - 1) / BK);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  int kt = 0;
+  for (; kt < nk - (STAGES - 1); ++kt) {
+    wait_vm<4 * (STAGES - 2)>();
+    __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; slot of kt-1 free
+    issue(kt + STAGES - 1);
+    compute(kt);
+    wait_lgkm0();  // this stage's fragment reads done before its slot is refilled
   }
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) {
+    if (kt < nk) {
+      if (t == 0) wait_vm<4 * (STAGES - 2)>();
+      else if (t == 1) wait_vm<4 * (STAGES - 3)>();
+      else wait_vm<0>();
+      __builtin_amdgcn_s_barrier();
+      compute(kt);
+      wait_lgkm0();
+    }
+    ++kt;
+  }
+  wait_vm<0>();
 
   // ---- add the two K halves: waves 4..7 hand their tiles to waves 0..3
-  __syncthreads();  // ring no longer read
+  __syncthreads();  // ring no longer read or written
   i32x4 *xch = reinterpret_cast<i32x4 *>(smem);
   if (kh == 1) {
 #pragma unroll
@@ -166,74 +194,96 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
       for (int j = 0; j < 4; ++j) xch[((wave - 4) * 16 + i * 4 + j) * 64 + lane] = acc[i][j];
   }
   __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] += xch[(wave * 16 + i * 4 + j) * 64 + lane];
 
-  // ---- epilogue. acc[i][j] lane holds D[4g + v][r] of MFMA tile (i, j).
+  // ---- epilogue into the LDS output tile (after the exchange area).
+  // acc[i][j] lane holds D[4g + v][r] of MFMA tile (i, j).
+  char *tl = smem + XCH_BYTES;
+  if (kh == 0) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 64 + j * 16 + r;
-    if (n >= N) continue;
-    if constexpr (EPI == EPI_RAW) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] += xch[(wave * 16 + i * 4 + j) * 64 + lane];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + v;
-          if (m < M) p.c[m * N + n] = acc[i][j][v];
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 64 + j * 16 + r;
+      const int64_t n = n0 + col;
+      const bool nin = n < N;
+      if constexpr (EPI == EPI_RAW) {
+        int *t = reinterpret_cast<int *>(tl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) t[(wm * 64 + i * 16 + 4 * g + v) * TILE_LD + col] = acc[i][j][v];
+      } else if constexpr (EPI == EPI_Q8TA) {
+        float *t = reinterpret_cast<float *>(tl);
+        const int ws = nin ? p.wsum[n] : 0;
+        const float wsc = nin ? p.wscale[n] : 0.0f;
+        const float b = (nin && p.bias) ? p.bias[n] : 0.0f;
+        // sum_k (xq - z) q = acc - z * wsum fits int32 (|.| <= K * 255 * 128); the
+        // intermediate terms are formed in wrapping unsigned arithmetic.
+        const uint32_t zw1 = (uint32_t)p.z1 * (uint32_t)ws, zw2 = (uint32_t)p.z2 * (uint32_t)ws;
+        if constexpr (TWO) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float f = p.s1 * (float)(int)((uint32_t)acc[i][j][v] - zw1) +
+                              p.s2 * (float)(int)((uint32_t)acc[i + 2][j][v] - zw2);
+              t[(wm * 32 + i * 16 + 4 * g + v) * TILE_LD + col] = wsc * f + b;
+            }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              t[(wm * 64 + i * 16 + 4 * g + v) * TILE_LD + col] =
+                  wsc * (p.s1 * (float)(int)((uint32_t)acc[i][j][v] - zw1)) + b;
         }
-    } else if constexpr (EPI == EPI_Q8TA) {
-      const int ws = p.wsum[n];
-      const float wsc = p.wscale[n];
-      const float b = p.bias ? p.bias[n] : 0.0f;
-      // sum_k (xq - z) q = acc - z * wsum fits int32 (|.| <= K * 255 * 128); the
-      // intermediate terms are formed in wrapping unsigned arithmetic.
-      const uint32_t zw1 = (uint32_t)p.z1 * (uint32_t)ws, zw2 = (uint32_t)p.z2 * (uint32_t)ws;
-      if constexpr (TWO) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + wm * 32 + i * 16 + 4 * g + v;
-            if (m >= M) continue;
-            const float f = p.s1 * (float)(int)((uint32_t)acc[i][j][v] - zw1) +
-                            p.s2 * (float)(int)((uint32_t)acc[i + 2][j][v] - zw2);
-            p.y[m * N + n] = wsc * f + b;
-          }
-      } else {
+      } else {  // EPI_DQ8
+        float *t = reinterpret_cast<float *>(tl);
+        const int ws = nin ? p.wsum[n] : 0;
+        const float wsc = nin ? p.wscale[n] : 0.0f;
+        const float b = (nin && p.bias) ? p.bias[n] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + v;
-            if (m >= M) continue;
-            p.y[m * N + n] = wsc * (p.s1 * (float)(int)((uint32_t)acc[i][j][v] - zw1)) + b;
+            const int row = wm * 64 + i * 16 + 4 * g + v;
+            const int64_t m = m0 + row;
+            const bool min_ = m < M;
+            const int xz = min_ ? p.xz[m] : 0;
+            const float xs = min_ ? p.xs[m] : 0.0f;
+            const int A = (int)((uint32_t)acc[i][j][v] - (uint32_t)xz * (uint32_t)ws);
+            t[row * TILE_LD + col] = xs * (wsc * (float)A) + b;
           }
       }
-    } else {  // EPI_DQ8
-      const int ws = p.wsum[n];
-      const float wsc = p.wscale[n];
-      const float b = p.bias ? p.bias[n] : 0.0f;
+    }
+  }
+  __syncthreads();
+
+  // ---- write the tile: 32 lanes x 16 B per row
+  const bool vec = (N & 3) == 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+  for (int s = 0; s < MROWS / 16; ++s) {
+    const int u = tid + 512 * s, row = u >> 5, c = u & 31;
+    const int64_t m = m0 + row, n = n0 + 4 * c;
+    if (m >= M || n >= N) continue;
+    const i32x4 val = *reinterpret_cast<const i32x4 *>(tl + (row * TILE_LD + 4 * c) * 4);
+    int *dst = EPI == EPI_RAW ? p.c + m * N + n : reinterpret_cast<int *>(p.y + m * N + n);
+    if (vec) {
+      *reinterpret_cast<i32x4 *>(dst) = val;
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t m = m0 + wm * 64 + i * 16 + 4 * g + v;
-          if (m >= M) continue;
-          const int A = (int)((uint32_t)acc[i][j][v] - (uint32_t)p.xz[m] * (uint32_t)ws);
-          p.y[m * N + n] = p.xs[m] * (wsc * (float)A) + b;
-        }
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) dst[e] = val[e];
     }
   }
 }
 
 template <int EPI, bool TWO>
 hipError_t launch_one(const GemmArgs &a, int tiles_m, int tiles_n, hipStream_t st) {
-  // 128 KB of dynamic LDS: raise the function's limit (idempotent; on a runtime
-  // that does not need it the call's status is irrelevant, the launch reports).
+  // More than 64 KB of dynamic LDS: raise the function's limit once. Its status
+  // is not needed: a launch the limit does not allow reports its own error.
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void *)k_gemm_i8<EPI, TWO>,

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
 // chunks XOR-swizzled by row mod 8, nibble rows by row mod 4.
 namespace {
 constexpr int TB = 64;                          // tile rows and columns
-constexpr int Q_STAGES = 4;
+constexpr int Q_STAGES = 3;
 constexpr int QA_BYTES = TB * 128;              // xq: 128 k
 constexpr int QB_BYTES = TB * 64;               // nibbles: 128 k
 constexpr int QG_BYTES = TB * 16;               // 4 group scales (or sums) per row
@@ -224,7 +224,7 @@ constexpr int Q_STAGE = QA_BYTES + QB_BYTES + 2 * QG_BYTES;  // 14 KB
 constexpr int Q_DUMMY = Q_STAGES * Q_STAGE;     // scratch slot for padding loads
 constexpr int Q_LDS = Q_DUMMY + 1024;
 constexpr int Q_TILE_LD = TB + 4;               // words per staged output row
-static_assert(TB * Q_TILE_LD * 4 + 2 * 4 * 64 * 16 * 4 <= Q_DUMMY, "epilogue fits in the ring");
+static_assert(TB * Q_TILE_LD * 4 + 4 * 4 * 64 * 16 <= Q_DUMMY, "epilogue (tile + half-sum exchange) fits in the ring");
 }  // namespace
 
 // Kind of a wave's q-th load per stage (see the kernel): xq, nibbles,
@@ -237,7 +237,7 @@ __host__ __device__ constexpr int q4_load_kind(int q) {
 }
 
 template <int KH>
-__global__ __launch_bounds__(256 * KH) void k_dq8ca_q4_tiled(Q4Args p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(256 * KH, 2 / KH) void k_dq8ca_q4_tiled(Q4Args p, int tiles_m, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NW = 4 * KH, NL = 24 / NW;  // waves, loads per wave per stage
   const int nt = tiles_m * tiles_n;

@@ -94,7 +94,7 @@ struct GroupHeader {
   int32_t count;         // entries that follow (non-empty problems)
   int32_t total_blocks;  // grid size
   int32_t waves;         // waves per workgroup
-  int32_t mblocks;       // 4-row blocks of x per tile
+  int32_t mblocks;       // 4-row blocks of x per tile (0: single-row tile)
   int32_t tgroups;       // 4-channel groups per tile
   int32_t reserved[9];
 };
@@ -283,7 +283,7 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   const GroupHeader *h = static_cast<const GroupHeader *>(table);
   REQUIRE(h->magic == kGroupMagic && h->version == 1 && h->count >= 0 && h->total_blocks >= 0 &&
               (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8) &&
-              (h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4) &&
+              (h->mblocks == 0 || h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4) &&
               (h->tgroups == 1 || h->tgroups == 2 || h->tgroups == 4),
           AQL_ERR_PARAM, "%s: table was not written by aql_w8a16_group_plan", fn);
   if (h->count == 0 || h->total_blocks == 0) return ok();

@@ -43,7 +43,8 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
                         hipStream_t st);
 
 // Launch shape of the W8A16 kernel: waves per workgroup, groups of 4 output
-// channels per tile (1, 2 or 4) and blocks of 4 rows of x per tile (1, 2 or 4).
+// channels per tile (1, 2 or 4) and blocks of 4 rows of x per tile (1, 2 or 4;
+// 0 selects the single-row tile, M = 1).
 struct W8A16Shape {
   int waves, tgroups, mblocks;
 };

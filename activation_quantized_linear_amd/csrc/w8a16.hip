@@ -65,11 +65,103 @@ struct Tile {
 };
 
 // LDS for the cross-wave reduction: per wave, per (row group, m block), per
-// column j, four rows of x.
+// column j, four rows of x. MB = 0 is the single-row (M = 1) tile.
 template <int W, int TG, int MB>
 struct Red {
-  f32x4 v[W][TG][MB][4];
+  f32x4 v[W][TG][MB > 0 ? MB : 1][4];
 };
+
+// M = 1: each lane loads 8 contiguous bytes of x per step (4 bf16: the wave
+// reads the step's 512 bytes with one instruction), k-quarter i = lane % 4 of
+// its block's 16-element slice, and uses it as the A operand row i for all
+// four k-quarters e of the weights. Block b then computes D[i][j] = x_i . w_e(j),
+// which is wanted only for i = e, so each e accumulates separately and the
+// wanted value of accumulator e sits in its VGPR e.
+template <int W, int TG, int U>
+__device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W, TG, 0> &red) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, blk = lane >> 2;
+  const int64_t K = t.K;
+  const int64_t nrows = t.N - t.n0 < 4 * TG ? t.N - t.n0 : 4 * TG;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(t.q + t.n0 * K, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(t.x + t.m0 * K, (uint32_t)(K * 2));
+  const uint32_t qlane = (uint32_t)(j * K + 16 * blk);
+  const uint32_t xlane = 8u * (uint32_t)lane;
+  const int nst = (int)((K + 255) >> 8);
+  const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
+
+  f32x4 acc[TG][4];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[tg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto fetch = [&](int i0, i32x4 (*w_)[TG], i32x2 *x_) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      const int st = wave + W * i;
+      const bool valid = i < cnt;  // uniform
+      const bool kin = (256 * st + 16 * blk) < K;
+      const uint32_t qstep = valid ? 256u * st : (uint32_t)OOB;
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg) {
+        const int qo = (int)(qlane + (uint32_t)(4 * tg) * (uint32_t)K + qstep);
+        w_[u][tg] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
+      }
+      const int xo = (valid && kin) ? (int)(xlane + 512u * st) : OOB;
+      x_[u] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0));
+    }
+  };
+  auto mul = [&](i32x4 (*w_)[TG], i32x2 *x_) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const s16x4 a = __builtin_bit_cast(s16x4, x_[u]);
+#pragma unroll
+      for (int tg = 0; tg < TG; ++tg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[tg][e] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, widen4(w_[u][tg][e]), acc[tg][e], 0, 0, 0);
+    }
+  };
+
+  i32x4 w0[U][TG], w1[U][TG];
+  i32x2 x0[U], x1[U];
+  fetch(0, w0, x0);
+  for (int b = 0; b < cnt; b += 2 * U) {
+    fetch(b + U, w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(b + 2 * U, w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  float v[TG];
+#pragma unroll
+  for (int tg = 0; tg < TG; ++tg) {
+    v[tg] = (acc[tg][0][0] + acc[tg][1][1]) + (acc[tg][2][2] + acc[tg][3][3]);
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) v[tg] += __shfl_xor(v[tg], o);
+  }
+  if (lane < 4) {
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) red.v[wave][tg][0][j] = f32x4{v[tg], 0.f, 0.f, 0.f};
+  }
+  if constexpr (W > 1) __syncthreads();
+  if (wave != 0 || lane >= 4 * TG) return;
+  const int tg = lane >> 2, jj = lane & 3;
+  const int64_t n = t.n0 + lane;
+  if (n >= t.N) return;
+  float sum = red.v[0][tg][0][jj][0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) sum += red.v[w][tg][0][jj][0];
+  const float bv = t.bias ? bf16_to_f32(t.bias[n]) : 0.0f;
+  t.y[t.m0 * t.N + n] = f32_to_bf16_rne(t.scale[n] * sum + bv);
+}
 
 // TG row groups of 4 output channels per tile (4 TG channels), MB blocks of 4
 // rows of x, W waves, U steps per fetched batch.
@@ -207,7 +299,8 @@ __global__ __launch_bounds__(64 * W) void k_w8a16(const uint16_t *__restrict__ x
   __shared__ Red<W, TG, MB> red;
   const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 4 * TG,
                (int64_t)blockIdx.y * 16};
-  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
+  if constexpr (MB == 0) w8a16_tile_m1<W, TG, 2>(t, red);
+  else w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
 }
 
 // Grouped launch: blocks [begin, begin + nblk * mblk) of the grid belong to
@@ -228,7 +321,8 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry 
   const int nb = local % e.nblk, mb = local / e.nblk;
   const Tile t{e.x, e.q, e.scale, e.bias, e.y, e.M, e.N, e.K, (int64_t)nb * 4 * TG,
                (int64_t)mb * 16};
-  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
+  if constexpr (MB == 0) w8a16_tile_m1<W, TG, 2>(t, red);
+  else w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
 }
 
 template <int TG, int MB>
@@ -264,6 +358,7 @@ void launch_single_tg(int MB, int W, dim3 grid, hipStream_t st, const uint16_t *
                       int64_t K, const int8_t *q, const float *scale, const uint16_t *bias,
                       int64_t N, uint16_t *y) {
   switch (MB) {
+    case 0: launch_single<TG, 0>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     case 1: launch_single<TG, 1>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     case 2: launch_single<TG, 2>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     default: launch_single<TG, 4>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
@@ -274,6 +369,7 @@ template <int TG>
 void launch_group_tg(int MB, int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab,
                      int count) {
   switch (MB) {
+    case 0: launch_group<TG, 0>(W, blocks, st, tab, count); break;
     case 1: launch_group<TG, 1>(W, blocks, st, tab, count); break;
     case 2: launch_group<TG, 2>(W, blocks, st, tab, count); break;
     default: launch_group<TG, 4>(W, blocks, st, tab, count); break;
@@ -283,17 +379,20 @@ void launch_group_tg(int MB, int W, int blocks, hipStream_t st, const W8A16Group
 }  // namespace
 
 // Launch shape, from a sweep of tile rows x waves on the 7B MLP shapes and the
-// SmolVLM decode sweep: streaming is fastest with few waves per workgroup (no
-// cross-wave reduction) and on the order of a thousand or more wave-tiles in
-// flight; 8-channel tiles suit M <= 2, 16-channel tiles larger M.
+// SmolVLM decode sweep: streaming is fastest with few waves per workgroup and
+// enough wave-tiles in flight: for the single-row tile about 3000 (8-channel
+// tiles; waves split K only while the tiles alone fall short), for larger M
+// about 768 (8-channel tiles for M <= 2, 16 otherwise).
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
   W8A16Shape s;
-  s.mblocks = M <= 4 ? 1 : (M <= 8 ? 2 : 4);
+  s.mblocks = M == 1 ? 0 : (M <= 4 ? 1 : (M <= 8 ? 2 : 4));
   s.tgroups = M <= 2 ? 2 : 4;
   const int64_t nst = (K + 255) / 256;  // 256-byte K steps
   const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
+  const int64_t want = M == 1 ? 3072 : 768;
+  const int wmax = M == 1 ? 8 : 16;
   int W = 1;
-  while (W < 16 && tiles * W < 768 && W * 4 <= nst) W <<= 1;
+  while (W < wmax && tiles * W < want && W * (M == 1 ? 2 : 4) <= nst) W <<= 1;
   s.waves = W;
   return s;
 }

@@ -187,7 +187,7 @@ def test_group_plan_validation():
     hdr = buf[:32].view(np.int32)
     rows = 4 * hdr[6]  # channels per tile (header: magic, version, count, blocks, waves, mblocks, tgroups)
     assert hdr[2] == 3 and hdr[3] == 3 * (-(-32 // rows))  # 3 problems of N = 32, M = 1
-    assert hdr[4] in (1, 2, 4, 8) and hdr[5] == 1
+    assert hdr[4] in (1, 2, 4, 8) and hdr[5] == 0  # M = 1: the single-row tile
     assert f(C.cast(_problems(3), C.c_void_p), 3, tp, nb - 1) == aql.AQL_ERR_WORKSPACE
     assert f(C.cast(_problems(3), C.c_void_p), 0, tp, nb) == aql.AQL_ERR_SHAPE
     assert f(C.cast(_problems(3, {1: dict(K=40)}), C.c_void_p), 3, tp, nb) == aql.AQL_ERR_SHAPE

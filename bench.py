@@ -29,8 +29,10 @@ cpu_baseline: the CPU oracle (test infrastructure; its only use here) timed on
 the host on a bounded sample of the headline workload.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -43,6 +45,10 @@ METRIC = "W8A16 decode GEMV GB/s (% HBM peak); W8A8 prefill GEMM TOPS (% int8 MF
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 MALL_BYTES = 256 << 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = "k_w8a16_grouped_smolvlm_decode_sweep_traffic.md"
+HEADLINE_SOURCES = ("activation_quantized_linear_amd/csrc/w8a16.hip",
+                    "activation_quantized_linear_amd/csrc/common.h")
 
 
 def parse():
@@ -55,7 +61,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline")
     ap.add_argument("--only", default=None,
-                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant)")
+                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant|copy)")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="profile helper: skip the settle phase (counter runs serialize every "
+                         "dispatch, so settling there only costs time)")
     return ap.parse_args()
 
 
@@ -86,12 +95,17 @@ def event_time_ms(torch, fn, reps, rotate, trials=5):
     return statistics.median(res), res
 
 
+_NO_SETTLE = [False]
+
+
 def settle(torch, fn, gpu_ms=50.0):
     """Run fn back to back for about gpu_ms of GPU time before anything is
     warmed up or timed. Coming out of idle the GPU streams memory measurably
     slower for the first 10-20 ms of sustained load (kernel durations of the
     same launch fall by about 10% and then stay flat), so a run is brought to
     that steady state once, at setup, rather than inside the timed region."""
+    if _NO_SETTLE[0]:
+        return 0
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     done, i = 0.0, 0
@@ -347,8 +361,46 @@ def cpu_baseline(layers, seconds):
                       f"{el:.1f} s on the host"}
 
 
+def sec_copy(torch, aql, workloads, dev, mib=256, reps=20):
+    """Reference row: a plain device-to-device copy of `mib` MiB (torch copy_),
+    the known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib << 20
+    src = torch.full((n,), 7, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    med, _ = event_time_ms(torch, lambda i: dst.copy_(src), reps, 1)
+    return [{"workload": f"device copy {mib} MiB (torch copy_)", "us": med * 1e3,
+             "bytes_read": n, "bytes_written": n, "GB/s": 2 * n / (med * 1e-3) / 1e9}]
+
+
+def sources_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name, sources):
+    """HBM bytes per launch of the headline kernel as measured by the FETCH_SIZE /
+    WRITE_SIZE counter runs summarized in profiles/<name> (each scaled by the
+    same counter on a plain copy of known size). The summary records a digest
+    of the kernel's sources; if they have changed since, the figure no longer
+    describes this kernel and None is returned."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    m_d = re.search(r"^sources_sha256_16:\s*([0-9a-f]+)", text, re.M)
+    if not (m_b and m_d) or m_d.group(1) != sources_digest(sources):
+        return None
+    return int(m_b.group(1))
+
+
 def main():
     args = parse()
+    _NO_SETTLE[0] = args.no_settle
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures a single GPU (got --gpus {args.gpus}, WORLD_SIZE {world}): the "
@@ -368,7 +420,8 @@ def main():
 
     secondary = []
     if args.only is not None and args.only != "sweep":
-        fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant}[args.only]
+        fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant,
+              "copy": sec_copy}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
         return
     calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
@@ -415,7 +468,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": value / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": traffic_from_profile(TRAFFIC_PROFILE, HEADLINE_SOURCES),
             "kernel": "k_w8a16_grouped",
             "bytes_per_launch": step_bytes,
             "avg_launch_us": ms * 1e3,

@@ -192,21 +192,38 @@ __device__ __forceinline__ float act_code(float v, float inv, float z) {
   return clamp_code(rintf(v * inv) + z, -128.0f, 127.0f);
 }
 
+// A wave handles 256 float4 (4 KB) per round: 4 loads of 64 lanes x 16 B, each
+// a contiguous 1 KB, all in flight before any code is formed; each load's 64
+// codes go out as one contiguous 256-byte store per pass.
 template <bool TWO>
 __global__ __launch_bounds__(256) void k_quantize_act_per_tensor(
     const float4 *__restrict__ x, int64_t nvec, float s1, float inv1, float z1, float inv2,
     float z2, uint32_t *__restrict__ xq1, uint32_t *__restrict__ xq2) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    const float4 v = x[i];
-    const float a = act_code(v.x, inv1, z1), b = act_code(v.y, inv1, z1);
-    const float c = act_code(v.z, inv1, z1), d = act_code(v.w, inv1, z1);
-    xq1[i] = pack4((int)a, (int)b, (int)c, (int)d);
-    if constexpr (TWO) {
-      const float ra = v.x - (a - z1) * s1, rb = v.y - (b - z1) * s1;
-      const float rc = v.z - (c - z1) * s1, rd = v.w - (d - z1) * s1;
-      xq2[i] = pack4((int)act_code(ra, inv2, z2), (int)act_code(rb, inv2, z2),
-                     (int)act_code(rc, inv2, z2), (int)act_code(rd, inv2, z2));
+  const int lane = threadIdx.x & 63;
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t base = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 256;
+       base < nvec; base += nw * 256) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + 64 * u + lane;
+      const f32x4 t = i < nvec ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + i))
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[u] = make_float4(t[0], t[1], t[2], t[3]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = base + 64 * u + lane;
+      if (i >= nvec) continue;
+      const float a = act_code(v[u].x, inv1, z1), b = act_code(v[u].y, inv1, z1);
+      const float c = act_code(v[u].z, inv1, z1), d = act_code(v[u].w, inv1, z1);
+      xq1[i] = pack4((int)a, (int)b, (int)c, (int)d);
+      if constexpr (TWO) {
+        const float ra = v[u].x - (a - z1) * s1, rb = v[u].y - (b - z1) * s1;
+        const float rc = v[u].z - (c - z1) * s1, rd = v[u].w - (d - z1) * s1;
+        xq2[i] = pack4((int)act_code(ra, inv2, z2), (int)act_code(rb, inv2, z2),
+                       (int)act_code(rc, inv2, z2), (int)act_code(rd, inv2, z2));
+      }
     }
   }
 }
@@ -344,8 +361,9 @@ hipError_t launch_quantize_act_per_tensor(const float *x, int64_t count, float s
   const int64_t nvec = count / 4;
   const float inv1 = 1.0f / s1;
   const float inv2 = two_pass ? 1.0f / s2 : 0.0f;
-  int64_t blocks = (nvec + 255) / 256;
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  // one wave per 256 float4, at most 16 waves per CU (the rest grid-strides)
+  int64_t blocks = (nvec + 1023) / 1024;
+  if (blocks > 256 * 4) blocks = 256 * 4;
   if (blocks < 1) blocks = 1;
   if (two_pass)
     hipLaunchKernelGGL(k_quantize_act_per_tensor<true>, dim3((unsigned)blocks), dim3(256), 0, st,

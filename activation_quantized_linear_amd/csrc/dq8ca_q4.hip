@@ -36,7 +36,7 @@ __device__ __forceinline__ long unpack_q4x8(uint32_t w) {
   return (long)((uint64_t)even | ((uint64_t)odd << 32));
 }
 
-// --------------------------------------------------------- skinny (M <= 16)
+// ------------------------------------------------------ streaming (M <= 16)
 // Bound by streaming the packed weights (and their group scales and sums) from
 // HBM. The access shape follows the weight-only GEMV: a wave instruction reads
 // 4 weight rows x 256 contiguous bytes, so each lane holds 16 bytes = one whole

@@ -66,6 +66,8 @@ _SIGS = {
     "aql_linear_dq8ca": ([_p, _i64, _i64, _int, _p, _p, _p, _int, _p, _i64, _p, _p, _p, _p, _sz,
                           _p], _int),
     "aql_gemm_i8_i32": ([_p, _p, _p, _i64, _i64, _i64, _p], _int),
+    "aql_measure_read": ([_p, _i64, _p, _p], _int),
+    "aql_measure_mfma_i8": ([_i64, _p, _p], _int),
     "aql_w8a16_group_table_bytes": ([_int], _sz),
     "aql_w8a16_group_plan": ([_p, _int, _p, _sz], _int),
     "aql_linear_w8a16_grouped": ([_p, _p, _p], _int),
@@ -303,6 +305,24 @@ def aql_linear_dq8ca(x, wq, wscale, wsum, wfmt=AQL_W_Q8CSW, group=0, bias=None, 
                                  int(group), _ptr(bias), N, _ptr(y), _ptr(x_scale_out),
                                  _ptr(x_zp_out), _ptr(ws), ws.numel(), _stream(dev)))
     return y
+
+
+def aql_measure_read(buf, sink):
+    """Measurement helper: one launch that reads all of `buf` (a contiguous
+    device tensor whose byte size is a multiple of 1024) as a read-only HBM
+    stream. sink: a device tensor of at least 4 bytes."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check("aql_measure_read", _lib.aql_measure_read(_ptr(buf), nbytes, _ptr(sink),
+                                                     _stream(buf.device)))
+
+
+def aql_measure_mfma_i8(iters, sink):
+    """Measurement helper: 2048 waves x 16 * iters int8 16x16x64 MFMAs
+    (2048 * 32768 * 16 * iters integer ops)."""
+    _check("aql_measure_mfma_i8", _lib.aql_measure_mfma_i8(int(iters), _ptr(sink),
+                                                           _stream(sink.device)))
 
 
 def aql_gemm_i8_i32(a, b, c=None):

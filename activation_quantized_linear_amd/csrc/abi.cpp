@@ -12,6 +12,7 @@
 
 #include "aql.h"
 #include "common.h"
+#include "measure.h"
 
 namespace {
 
@@ -437,6 +438,27 @@ int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int
   g.N = N;
   g.K = K;
   return launched(aql::launch_gemm_i8(g, aql::EPI_RAW, false, (hipStream_t)stream), fn);
+}
+
+int aql_measure_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {
+  const char *fn = "aql_measure_read";
+  REQUIRE(buf && sink, AQL_ERR_NULL, "%s: buf and sink must not be NULL", fn);
+  REQUIRE(aligned16(buf) && aligned16(sink), AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned",
+          fn);
+  REQUIRE(bytes >= 1024 && bytes % 1024 == 0 && bytes <= (1LL << 31) - 1024, AQL_ERR_SHAPE,
+          "%s: bytes must be a multiple of 1024 in [1024, 2^31 - 1024] (got %lld)", fn,
+          (long long)bytes);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_measure_read(buf, bytes, sink, (hipStream_t)stream), fn);
+}
+
+int aql_measure_mfma_i8(int64_t iters, int32_t *sink, void *stream) {
+  const char *fn = "aql_measure_mfma_i8";
+  REQUIRE(sink, AQL_ERR_NULL, "%s: sink must not be NULL", fn);
+  REQUIRE(aligned16(sink), AQL_ERR_ALIGN, "%s: sink must be 16-byte aligned", fn);
+  REQUIRE(iters >= 1 && iters <= (1LL << 30), AQL_ERR_SHAPE, "%s: iters must be in [1, 2^30]", fn);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_measure_mfma_i8(iters, sink, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

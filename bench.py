@@ -390,6 +390,28 @@ def sec_copy(torch, aql, workloads, dev, mib=256, reps=20):
              "bytes_read": n, "bytes_written": n, "GB/s": 2 * n / (med * 1e-3) / 1e9}]
 
 
+def ceilings(torch, aql, dev):
+    """Attainable ceilings on this GPU, measured in the same run: a read-only
+    HBM stream (two 512 MiB buffers rotated, so no read hits the 256 MB
+    Infinity Cache) and back-to-back int8 MFMAs on all CUs."""
+    n = 512 << 20
+    bufs = [torch.full((n,), 1, dtype=torch.uint8, device=dev) for _ in range(2)]
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    rd_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_read(bufs[i], sink), 10, 2)
+    del bufs
+    iters = 20000
+    ops = 2048 * 32768 * 16 * iters
+    mf_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_mfma_i8(iters, sink), 3, 1)
+    rd = n / (rd_ms * 1e-3) / 1e9
+    tops = ops / (mf_ms * 1e-3) / 1e12
+    out = {"hbm_read_GBs": rd, "hbm_read_frac": rd / HBM_PEAK_GBS,
+           "mfma_i8_TOPS": tops, "mfma_i8_frac": tops / INT8_PEAK_TOPS,
+           "how": "aql_measure_read over 512 MiB (2 buffers rotated); "
+                  "aql_measure_mfma_i8 (2048 waves x 16 x 20000 MFMAs)"}
+    say(out)
+    return out
+
+
 def sources_digest(files):
     h = hashlib.sha256()
     for f in files:
@@ -453,6 +475,11 @@ def main():
             secondary += fn(torch, aql, workloads, dev)
             torch.cuda.empty_cache()
 
+    ceil = None
+    if args.only is None and not args.no_secondary:
+        ceil = ceilings(torch, aql, dev)
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         say("cpu baseline ...")
@@ -493,6 +520,7 @@ def main():
             "launches_timed": args.steps,
         },
         "cpu_baseline": cpu,
+        "ceilings": ceil,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -300,6 +300,30 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
 int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);
 
+/* ---------------------------------------------------- measurement helpers */
+
+/*
+ * Not part of the method: the attainable ceilings the linears are measured
+ * against on this GPU (published peaks are HBM 8 TB/s and dense int8 MFMA
+ * 5.0 POP/s).
+ *
+ * aql_measure_read: one launch that reads `bytes` of device memory once
+ * (a read-only HBM stream in the fastest shape measured here: 1 KB per wave
+ * instruction, 8 in flight, nontemporal, 4 waves per CU). Time it with events
+ * to get the read ceiling; rotate buffers larger than the 256 MB Infinity
+ * Cache. sink: device, 4 bytes, written only in a case that does not arise for
+ * ordinary data (it keeps the loads from being optimized away).
+ * Errors: buf or sink NULL / misaligned; bytes < 1024, not a multiple of 1024,
+ * or above 2^31 - 1024.
+ *
+ * aql_measure_mfma_i8: one launch of 2 waves per SIMD on every CU (256 x 8
+ * waves), each issuing 16 * iters back-to-back v_mfma_i32_16x16x64_i8 (32768
+ * integer ops each) on register operands: 2048 * 32768 * 16 * iters ops in total.
+ * Errors: iters < 1 or > 2^30; sink NULL / misaligned.
+ */
+int aql_measure_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+int aql_measure_mfma_i8(int64_t iters, int32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

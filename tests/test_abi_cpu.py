@@ -147,6 +147,21 @@ def test_gemm_validation():
     assert f(A, B, Y, 0, 4, 64, None) == aql.AQL_OK
 
 
+def test_measure_helpers_validation():
+    r = L.aql_measure_read
+    assert r(NUL, 1024, Y, None) == aql.AQL_ERR_NULL
+    assert r(A, 1024, NUL, None) == aql.AQL_ERR_NULL
+    assert r(MIS, 1024, Y, None) == aql.AQL_ERR_ALIGN
+    assert r(A, 1000, Y, None) == aql.AQL_ERR_SHAPE
+    assert r(A, 0, Y, None) == aql.AQL_ERR_SHAPE
+    assert r(A, 1 << 31, Y, None) == aql.AQL_ERR_SHAPE
+    m = L.aql_measure_mfma_i8
+    assert m(0, Y, None) == aql.AQL_ERR_SHAPE
+    assert m((1 << 30) + 1, Y, None) == aql.AQL_ERR_SHAPE
+    assert m(4, NUL, None) == aql.AQL_ERR_NULL
+    assert m(4, MIS, None) == aql.AQL_ERR_ALIGN
+
+
 def test_valid_call_without_gpu_reports_device():
     """On a host without a gfx950, a valid non-empty call fails with
     AQL_ERR_DEVICE before launching anything."""

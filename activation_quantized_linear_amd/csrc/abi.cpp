@@ -13,6 +13,10 @@
 #include "aql.h"
 #include "common.h"
 #include "measure.h"
+#include "w8a16_gemm.h"
+
+// Rows of x from which aql_linear_w8a16 uses the tiled GEMM.
+constexpr int64_t kW8A16GemmMinM = 64;
 
 namespace {
 
@@ -213,6 +217,12 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
   if (int e = check_w8a16(fn, x, M, K, q, scale, bias, N, y)) return e;
   if (M == 0 || N == 0) return ok();
   if (int e = check_device(fn)) return e;
+  // M-dispatch (flashrt schemes, W8A16Decode: the decode band goes to the
+  // weight-streaming kernel): from 64 rows on, the tiled bf16-MFMA GEMM reads
+  // each weight once per 64 or 128 rows instead of once per 16.
+  if (M >= kW8A16GemmMinM && K <= (1LL << 22))
+    return launched(aql::launch_w8a16_gemm(x, M, K, q, scale, bias, N, y, (hipStream_t)stream),
+                    fn);
   return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
 }
 

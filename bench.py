@@ -46,6 +46,7 @@ if ROOT not in sys.path:
 METRIC = "W8A16 decode GEMV GB/s (% HBM peak); W8A8 prefill GEMM TOPS (% int8 MFMA)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = "k_w8a16_grouped_smolvlm_decode_sweep_traffic.md"
@@ -246,18 +247,21 @@ def sec_llm7b(torch, aql, workloads, dev):
         del d
         ncopy = copies_for(N * K)
         qs = [q] + [q.clone() for _ in range(ncopy - 1)]
-        for M in (1, 4, 16):
+        for M in (1, 4, 16, 512, 2048):
             x = workloads.llm7b(K, 16, M, seed=3)["x"].to(dev)
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
             fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
             for i in range(ncopy):
                 fn(i)
-            med, _ = event_time_ms(torch, fn, 50, ncopy)
+            med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N
             gbs = nb / (med * 1e-3) / 1e9
-            rows.append({"workload": f"llm7b_w8a16 K={K} N={N} M={M}", "us": med * 1e3,
-                         "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                         "TFLOP/s": 2 * M * N * K / (med * 1e-3) / 1e12})
+            tf = 2 * M * N * K / (med * 1e-3) / 1e12
+            row = {"workload": f"llm7b_w8a16 K={K} N={N} M={M}", "us": med * 1e3,
+                   "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS, "TFLOP/s": tf}
+            if M > 16:  # prefill: the tiled bf16-MFMA GEMM
+                row["frac_bf16"] = tf / BF16_PEAK_TFLOPS
+            rows.append(row)
             say(rows[-1])
         del qs, q
     return rows

@@ -239,6 +239,37 @@ def test_w8a16_smolvlm_sweep():
             check_float(y, yref, tol, BF16, f"layer {li} {wname}")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 128, 64), (65, 129, 80), (128, 300, 1040), (200, 257, 4096),
+                                   (513, 130, 272), (1024, 2048, 512)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a16_prefill_shapes(M, N, K, with_bias):
+    """Prefill-sized M runs the tiled bf16-MFMA GEMM (64- or 128-row tiles):
+    ragged M, N and K (K % 64 != 0), with and without bias."""
+    say("w8a16 prefill", M, N, K, with_bias)
+    g = workloads.gen(700 + M + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+    b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16) if with_bias else None
+    w[1] = 0.0
+    y, yref, tol = _w8a16_case(x, w, b)
+    check_float(y, yref, tol, BF16, f"w8a16 prefill {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
+def test_w8a16_llm7b_prefill_full_size(K, N):
+    """7B shapes at M = 512 (the tiled GEMM at its real size), checked on
+    sampled rows: the first and last rows and 6 random ones."""
+    M = 512
+    say("w8a16 7b prefill", K, N, M)
+    d = workloads.llm7b(K, N, M, seed=6)
+    q, s, _ = aql.aql_quantize_weight_int8(dev(d["w"]), aql.AQL_WQ_SYM127)
+    y = host(aql.aql_linear_w8a16(dev(d["x"]), q, s).float())
+    rng = np.random.default_rng(K + N)
+    rows = np.r_[0, M - 1, rng.choice(np.arange(1, M - 1), 6, replace=False)]
+    yref, tol = oracle.linear_w8a16(bits(d["x"][rows]), host(q), host(s), None)
+    check_float(y[rows], yref, tol, BF16, f"7b prefill {K}x{N}")
+
+
 @pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_w8a16_llm7b_full(K, N, M):

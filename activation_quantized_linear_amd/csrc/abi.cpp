@@ -101,7 +101,9 @@ struct GroupHeader {
   int32_t waves;         // waves per workgroup
   int32_t mblocks;       // 4-row blocks of x per tile (0: single-row tile)
   int32_t tgroups;       // 4-channel groups per tile
-  int32_t reserved[9];
+  int32_t cgroups;       // wave tiles per workgroup along N (single-row tile)
+  int32_t xlds;          // LDS bytes holding x (single-row tile; 0: none)
+  int32_t reserved[7];
 };
 static_assert(sizeof(GroupHeader) == 64, "table header");
 constexpr uint32_t kGroupMagic = 0x47514c41u;  // "ALQG"
@@ -241,7 +243,7 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
   GroupHeader *h = static_cast<GroupHeader *>(table);
   aql::W8A16GroupEntry *e = reinterpret_cast<aql::W8A16GroupEntry *>(h + 1);
   // One launch shape for the whole group, from the smallest K and the largest M.
-  int64_t kmin = 0, mmax = 0, nsum = 0;
+  int64_t kmin = 0, kmax = 0, mmax = 0, nsum = 0;
   for (int i = 0; i < count; ++i) {
     const aql_w8a16_problem &p = problems[i];
     char name[64];
@@ -249,12 +251,15 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
     if (int rc = check_w8a16(name, p.x, p.M, p.K, p.q, p.scale, p.bias, p.N, p.y)) return rc;
     if (p.M == 0 || p.N == 0) continue;
     kmin = (kmin == 0 || p.K < kmin) ? p.K : kmin;
+    kmax = p.K > kmax ? p.K : kmax;
     mmax = p.M > mmax ? p.M : mmax;
     nsum += p.N * ((p.M + 15) / 16);
   }
   aql::W8A16Shape sh = aql::w8a16_shape(mmax ? mmax : 1, nsum ? nsum : 1, kmin ? kmin : 16);
   if (sh.waves > 8) sh.waves = 8;
-  const int64_t rows = 4 * sh.tgroups;
+  // x shared through LDS only if every problem's x fits
+  if (sh.mblocks == 0) sh.xlds = aql::w8a16_xlds_bytes(kmax ? kmax : 16);
+  const int64_t rows = 4 * sh.tgroups * sh.cgroups;
   int64_t blocks = 0;
   int n = 0;
   for (int i = 0; i < count; ++i) {
@@ -279,12 +284,14 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
   }
   *h = GroupHeader{};
   h->magic = kGroupMagic;
-  h->version = 1;
+  h->version = 2;
   h->count = n;
   h->total_blocks = (int32_t)blocks;
   h->waves = sh.waves;
   h->mblocks = sh.mblocks;
   h->tgroups = sh.tgroups;
+  h->cgroups = sh.cgroups;
+  h->xlds = sh.xlds;
   return ok();
 }
 
@@ -292,10 +299,15 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   const char *fn = "aql_linear_w8a16_grouped";
   REQUIRE(table, AQL_ERR_NULL, "%s: table must not be NULL", fn);
   const GroupHeader *h = static_cast<const GroupHeader *>(table);
-  REQUIRE(h->magic == kGroupMagic && h->version == 1 && h->count >= 0 && h->total_blocks >= 0 &&
+  const bool m1 = h->mblocks == 0;
+  REQUIRE(h->magic == kGroupMagic && h->version == 2 && h->count >= 0 && h->total_blocks >= 0 &&
               (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8) &&
               (h->mblocks == 0 || h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4) &&
-              (h->tgroups == 1 || h->tgroups == 2 || h->tgroups == 4),
+              (h->tgroups == 1 || h->tgroups == 2 || h->tgroups == 4) &&
+              (m1 ? (h->tgroups == 2 && (h->cgroups == 1 || h->cgroups == 2 || h->cgroups == 4) &&
+                     h->waves * h->cgroups <= 16 && h->xlds >= 0 &&
+                     h->xlds <= aql::kW8A16MaxXlds && h->xlds % 1024 == 0)
+                  : (h->cgroups == 1 && h->xlds == 0)),
           AQL_ERR_PARAM, "%s: table was not written by aql_w8a16_group_plan", fn);
   if (h->count == 0 || h->total_blocks == 0) return ok();
   REQUIRE(dev_table, AQL_ERR_NULL, "%s: dev_table must not be NULL", fn);
@@ -307,6 +319,8 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   sh.waves = h->waves;
   sh.mblocks = h->mblocks;
   sh.tgroups = h->tgroups;
+  sh.cgroups = h->cgroups;
+  sh.xlds = h->xlds;
   return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, sh,
                                             (hipStream_t)stream),
                   fn);

@@ -25,12 +25,15 @@
 // Launches: a single problem (grid = N/16 x M/16 tiles), or a group of
 // independent problems in one launch (a decode sweep's linears), whose tiles
 // are laid end to end in one grid and found through a device table.
+#include <type_traits>
+
 #include "common.h"
 
 namespace aql {
 namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int OOB = 0x40000000;  // an offset past any tile's range: loads return 0
 
@@ -71,25 +74,49 @@ struct Red {
   f32x4 v[W][TG][MB > 0 ? MB : 1][4];
 };
 
-// M = 1: each lane loads 8 contiguous bytes of x per step (4 bf16: the wave
-// reads the step's 512 bytes with one instruction), k-quarter i = lane % 4 of
-// its block's 16-element slice, and uses it as the A operand row i for all
-// four k-quarters e of the weights. Block b then computes D[i][j] = x_i . w_e(j),
+// M = 1: per step each lane takes 8 contiguous bytes of x (4 bf16; a wave's
+// 64 lanes cover the step's 512 bytes), k-quarter i = lane % 4 of its block's
+// 16-element slice, and uses it as the A operand row i for all four
+// k-quarters e of the weights. Block b then computes D[i][j] = x_i . w_e(j),
 // which is wanted only for i = e, so each e accumulates separately and the
 // wanted value of accumulator e sits in its VGPR e.
-template <int W, int TG, int U>
-__device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W, TG, 0> &red) {
+//
+// A workgroup holds CW wave tiles of 4 TG channels side by side along N, each
+// with W waves splitting K. With XL the workgroup first copies x (2 K bytes)
+// into LDS by direct buffer-to-LDS loads, so x is read from L2 once per
+// workgroup instead of once per wave tile, and each step reads its 8 bytes per
+// lane from LDS. The copy is issued before the first weight batch and waited
+// for after it, so its latency hides behind the weights'.
+template <int W, int CW, int TG, int U, bool XL>
+__device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W * CW, TG, 0> &red,
+                                              uint8_t *xs) {
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = wid / W, wave = wid % W;
   const int j = lane & 3, blk = lane >> 2;
   const int64_t K = t.K;
-  const int64_t nrows = t.N - t.n0 < 4 * TG ? t.N - t.n0 : 4 * TG;
-  const __amdgpu_buffer_rsrc_t rq = rsrc(t.q + t.n0 * K, (uint32_t)(nrows * K));
+  const int64_t n0 = t.n0 + 4 * TG * cw;
+  // a wave tile wholly past N gets an empty range (all its weight loads read 0)
+  const int64_t rem = t.N - n0;
+  const int64_t nrows = rem <= 0 ? 0 : (rem < 4 * TG ? rem : 4 * TG);
+  const __amdgpu_buffer_rsrc_t rq =
+      rsrc(nrows > 0 ? t.q + n0 * K : t.q, (uint32_t)(nrows * K));
   const __amdgpu_buffer_rsrc_t rx = rsrc(t.x + t.m0 * K, (uint32_t)(K * 2));
   const uint32_t qlane = (uint32_t)(j * K + 16 * blk);
   const uint32_t xlane = 8u * (uint32_t)lane;
   const int nst = (int)((K + 255) >> 8);
   const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
+
+  if constexpr (XL) {
+    // 1 KiB per wave instruction (16 bytes per lane); past 2 K the range check
+    // writes zeros, which the last step's lanes past K then read
+    const int nch = (int)((2 * K + 1023) >> 10);
+    const uint32_t base = (uint32_t)(uintptr_t)xs;
+    for (int c = wid; c < nch; c += W * CW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + 1024u * c), 16,
+          (int)(16u * lane + 1024u * c), 0, 0, 0);
+  }
 
   f32x4 acc[TG][4];
 #pragma unroll
@@ -97,27 +124,38 @@ __device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W, TG, 0> &red)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[tg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto fetch = [&](int i0, i32x4 (*w_)[TG], i32x2 *x_) {
+  auto fetch_w = [&](int i0, i32x4 (*w_)[TG]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u;
-      const int st = wave + W * i;
-      const bool valid = i < cnt;  // uniform
-      const bool kin = (256 * st + 16 * blk) < K;
-      const uint32_t qstep = valid ? 256u * st : (uint32_t)OOB;
+      const int st = wave + W * (i0 + u);
+      const uint32_t qstep = i0 + u < cnt ? 256u * st : (uint32_t)OOB;  // uniform
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg) {
         const int qo = (int)(qlane + (uint32_t)(4 * tg) * (uint32_t)K + qstep);
         w_[u][tg] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
       }
-      const int xo = (valid && kin) ? (int)(xlane + 512u * st) : OOB;
-      x_[u] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0));
     }
   };
-  auto mul = [&](i32x4 (*w_)[TG], i32x2 *x_) {
+  auto fetch_x = [&](int i0, i32x2 *x_) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const s16x4 a = __builtin_bit_cast(s16x4, x_[u]);
+      const int st = wave + W * (i0 + u);
+      const bool valid = i0 + u < cnt;  // uniform
+      if constexpr (XL) {
+        // steps past the wave's last read a valid address; mul zeroes them
+        x_[u] = *reinterpret_cast<const i32x2 *>(xs + (valid ? 512u * st : 0u) + xlane);
+      } else {
+        const bool kin = (256 * st + 16 * blk) < K;
+        const int xo = (valid && kin) ? (int)(xlane + 512u * st) : OOB;
+        x_[u] = __builtin_bit_cast(i32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0));
+      }
+    }
+  };
+  auto mul = [&](int i0, i32x4 (*w_)[TG], i32x2 *x_) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const i32x2 xv = (!XL || i0 + u < cnt) ? x_[u] : i32x2{0, 0};  // uniform
+      const s16x4 a = __builtin_bit_cast(s16x4, xv);
 #pragma unroll
       for (int tg = 0; tg < TG; ++tg)
 #pragma unroll
@@ -126,19 +164,33 @@ __device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W, TG, 0> &red)
     }
   };
 
+  // The loop body runs at least once (a wave without steps multiplies zeros):
+  // the first batch is then used unconditionally and cannot be sunk past the
+  // wait below, whose count assumes its U TG loads were issued after the copy.
   i32x4 w0[U][TG], w1[U][TG];
   i32x2 x0[U], x1[U];
-  fetch(0, w0, x0);
-  for (int b = 0; b < cnt; b += 2 * U) {
-    fetch(b + U, w1, x1);
-    __builtin_amdgcn_sched_barrier(0);
-    mul(w0, x0);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(b + 2 * U, w0, x0);
-    __builtin_amdgcn_sched_barrier(0);
-    mul(w1, x1);
-    __builtin_amdgcn_sched_barrier(0);
+  fetch_w(0, w0);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (XL) {
+    static_assert(U * TG < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (U * TG));  // this wave's copies done
+    __builtin_amdgcn_s_barrier();                   // every wave's copies done
   }
+  fetch_x(0, x0);
+  int b = 0;
+  do {
+    fetch_w(b + U, w1);
+    fetch_x(b + U, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(b, w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_w(b + 2 * U, w0);
+    fetch_x(b + 2 * U, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(b + U, w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    b += 2 * U;
+  } while (b < cnt);
 
   float v[TG];
 #pragma unroll
@@ -147,18 +199,28 @@ __device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W, TG, 0> &red)
 #pragma unroll
     for (int o = 4; o < 64; o <<= 1) v[tg] += __shfl_xor(v[tg], o);
   }
-  if (lane < 4) {
+  if constexpr (W > 1) {
+    if (lane < 4) {
 #pragma unroll
-    for (int tg = 0; tg < TG; ++tg) red.v[wave][tg][0][j] = f32x4{v[tg], 0.f, 0.f, 0.f};
+      for (int tg = 0; tg < TG; ++tg) red.v[wid][tg][0][j] = f32x4{v[tg], 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
   }
-  if constexpr (W > 1) __syncthreads();
   if (wave != 0 || lane >= 4 * TG) return;
-  const int tg = lane >> 2, jj = lane & 3;
-  const int64_t n = t.n0 + lane;
+  const int64_t n = n0 + lane;
   if (n >= t.N) return;
-  float sum = red.v[0][tg][0][jj][0];
+  float sum;
+  if constexpr (W > 1) {
+    const int tg = lane >> 2, jj = lane & 3;
+    sum = red.v[wid][tg][0][jj][0];
 #pragma unroll
-  for (int w = 1; w < W; ++w) sum += red.v[w][tg][0][jj][0];
+    for (int w = 1; w < W; ++w) sum += red.v[wid + w][tg][0][jj][0];
+  } else {
+    // lane 4 tg + jj holds v[tg] of column jj (every lane of a column agrees)
+    sum = v[0];
+#pragma unroll
+    for (int tg = 1; tg < TG; ++tg) sum = (lane >> 2) == tg ? v[tg] : sum;
+  }
   const float bv = t.bias ? bf16_to_f32(t.bias[n]) : 0.0f;
   t.y[t.m0 * t.N + n] = f32_to_bf16_rne(t.scale[n] * sum + bv);
 }
@@ -290,25 +352,13 @@ constexpr int batch_steps() {
   return TG * MB <= 8 ? 2 : 1;
 }
 
-template <int W, int TG, int MB>
-__global__ __launch_bounds__(64 * W) void k_w8a16(const uint16_t *__restrict__ x, int64_t M,
-                                                  int64_t K, const int8_t *__restrict__ q,
-                                                  const float *__restrict__ scale,
-                                                  const uint16_t *__restrict__ bias, int64_t N,
-                                                  uint16_t *__restrict__ y) {
-  __shared__ Red<W, TG, MB> red;
-  const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 4 * TG,
-               (int64_t)blockIdx.y * 16};
-  if constexpr (MB == 0) w8a16_tile_m1<W, TG, 2>(t, red);
-  else w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
-}
+constexpr int M1_TG = 2;  // single-row tile: 8 channels per wave tile
+constexpr int M1_U = 2;   // steps per fetched batch
 
 // Grouped launch: blocks [begin, begin + nblk * mblk) of the grid belong to
 // problem p, n-block fastest. The table is read through the scalar cache.
-template <int W, int TG, int MB>
-__global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry *__restrict__ tab,
-                                                          int count) {
-  __shared__ Red<W, TG, MB> red;
+__device__ __forceinline__ Tile group_tile(const W8A16GroupEntry *__restrict__ tab, int count,
+                                           int64_t rows) {
   const int blk = blockIdx.x;
   int lo = 0, hi = count - 1;
   while (lo < hi) {  // last entry with begin <= blk
@@ -319,10 +369,48 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry 
   const W8A16GroupEntry &e = tab[lo];
   const int local = blk - e.blk_begin;
   const int nb = local % e.nblk, mb = local / e.nblk;
-  const Tile t{e.x, e.q, e.scale, e.bias, e.y, e.M, e.N, e.K, (int64_t)nb * 4 * TG,
-               (int64_t)mb * 16};
-  if constexpr (MB == 0) w8a16_tile_m1<W, TG, 2>(t, red);
-  else w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
+  return Tile{e.x, e.q, e.scale, e.bias, e.y, e.M, e.N, e.K, (int64_t)nb * rows, (int64_t)mb * 16};
+}
+
+template <int W, int TG, int MB>
+__global__ __launch_bounds__(64 * W) void k_w8a16(const uint16_t *__restrict__ x, int64_t M,
+                                                  int64_t K, const int8_t *__restrict__ q,
+                                                  const float *__restrict__ scale,
+                                                  const uint16_t *__restrict__ bias, int64_t N,
+                                                  uint16_t *__restrict__ y) {
+  __shared__ Red<W, TG, MB> red;
+  const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 4 * TG,
+               (int64_t)blockIdx.y * 16};
+  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(t, red);
+}
+
+template <int W, int TG, int MB>
+__global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry *__restrict__ tab,
+                                                          int count) {
+  __shared__ Red<W, TG, MB> red;
+  w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(group_tile(tab, count, 4 * TG), red);
+}
+
+// Single-row tile; dynamic LDS holds x when XL.
+template <int W, int CW, bool XL>
+__global__ __launch_bounds__(64 * W * CW, 4) void k_w8a16_m1(const uint16_t *__restrict__ x,
+                                                          int64_t K,
+                                                          const int8_t *__restrict__ q,
+                                                          const float *__restrict__ scale,
+                                                          const uint16_t *__restrict__ bias,
+                                                          int64_t N, uint16_t *__restrict__ y) {
+  __shared__ Red<W * CW, M1_TG, 0> red;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  const Tile t{x, q, scale, bias, y, 1, N, K, (int64_t)blockIdx.x * 4 * M1_TG * CW, 0};
+  w8a16_tile_m1<W, CW, M1_TG, M1_U, XL>(t, red, xs);
+}
+
+template <int W, int CW, bool XL>
+__global__ __launch_bounds__(64 * W * CW, 4) void k_w8a16_m1_grouped(
+    const W8A16GroupEntry *__restrict__ tab, int count) {
+  __shared__ Red<W * CW, M1_TG, 0> red;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  w8a16_tile_m1<W, CW, M1_TG, M1_U, XL>(group_tile(tab, count, 4 * M1_TG * CW), red, xs);
 }
 
 template <int TG, int MB>
@@ -358,7 +446,6 @@ void launch_single_tg(int MB, int W, dim3 grid, hipStream_t st, const uint16_t *
                       int64_t K, const int8_t *q, const float *scale, const uint16_t *bias,
                       int64_t N, uint16_t *y) {
   switch (MB) {
-    case 0: launch_single<TG, 0>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     case 1: launch_single<TG, 1>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     case 2: launch_single<TG, 2>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
     default: launch_single<TG, 4>(W, grid, st, x, M, K, q, scale, bias, N, y); break;
@@ -369,11 +456,33 @@ template <int TG>
 void launch_group_tg(int MB, int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab,
                      int count) {
   switch (MB) {
-    case 0: launch_group<TG, 0>(W, blocks, st, tab, count); break;
     case 1: launch_group<TG, 1>(W, blocks, st, tab, count); break;
     case 2: launch_group<TG, 2>(W, blocks, st, tab, count); break;
     default: launch_group<TG, 4>(W, blocks, st, tab, count); break;
   }
+}
+
+// Single-row launches: one switch over (W, CW, XL) serves both kernels; F is
+// called with the kernel's template arguments as constants.
+template <typename F>
+void m1_dispatch(int W, int CW, bool XL, F f) {
+#define AQL_M1(w, c)                                                     \
+  if (W == w && CW == c) {                                               \
+    if (XL) f(std::integral_constant<int, w>{}, std::integral_constant<int, c>{}, \
+              std::true_type{});                                         \
+    else f(std::integral_constant<int, w>{}, std::integral_constant<int, c>{},    \
+           std::false_type{});                                           \
+    return;                                                              \
+  }
+  AQL_M1(1, 1) AQL_M1(1, 2) AQL_M1(1, 4) AQL_M1(2, 1) AQL_M1(2, 2) AQL_M1(2, 4)
+  AQL_M1(4, 1) AQL_M1(4, 2) AQL_M1(4, 4) AQL_M1(8, 1) AQL_M1(8, 2)
+#undef AQL_M1
+}
+
+bool m1_shape_ok(const W8A16Shape &sh) {
+  const int w = sh.waves, c = sh.cgroups;
+  return (w == 1 || w == 2 || w == 4 || w == 8) && (c == 1 || c == 2 || c == 4) && w * c <= 16 &&
+         sh.xlds >= 0 && sh.xlds <= kW8A16MaxXlds && sh.xlds % 1024 == 0;
 }
 
 }  // namespace
@@ -382,7 +491,11 @@ void launch_group_tg(int MB, int W, int blocks, hipStream_t st, const W8A16Group
 // SmolVLM decode sweep: streaming is fastest with few waves per workgroup and
 // enough wave-tiles in flight: for the single-row tile about 3000 (8-channel
 // tiles; waves split K only while the tiles alone fall short), for larger M
-// about 768 (8-channel tiles for M <= 2, 16 otherwise).
+// about 768 (8-channel tiles for M <= 2, 16 otherwise). The single-row tile
+// reads x from LDS whenever 2 K fits the budget (one 1 KiB load per wave
+// instruction instead of 512 bytes per step and wave), and pairs wave tiles in
+// a workgroup only when the grid is large: sharing x then saves L2 reads, while
+// on smaller grids the halved workgroup count costs more than it saves.
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
   W8A16Shape s;
   s.mblocks = M == 1 ? 0 : (M <= 4 ? 1 : (M <= 8 ? 2 : 4));
@@ -394,12 +507,31 @@ W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
   int W = 1;
   while (W < wmax && tiles * W < want && W * (M == 1 ? 2 : 4) <= nst) W <<= 1;
   s.waves = W;
+  if (M == 1) {
+    s.cgroups = tiles * W >= 8192 ? 2 : 1;
+    s.xlds = w8a16_xlds_bytes(K);
+  }
   return s;
+}
+
+int w8a16_xlds_bytes(int64_t K) {
+  const int64_t b = (2 * K + 1023) / 1024 * 1024;
+  return b <= kW8A16MaxXlds ? (int)b : 0;
 }
 
 hipError_t launch_w8a16_shape(const W8A16Shape &sh, const uint16_t *x, int64_t M, int64_t K,
                               const int8_t *q, const float *scale, const uint16_t *bias,
                               int64_t N, uint16_t *y, hipStream_t st) {
+  if (sh.mblocks == 0) {
+    if (M != 1 || !m1_shape_ok(sh) || (sh.xlds && sh.xlds < 2 * K)) return hipErrorInvalidValue;
+    const int64_t rows = 4 * M1_TG * sh.cgroups;
+    const dim3 grid((unsigned)((N + rows - 1) / rows)), block(64 * sh.waves * sh.cgroups);
+    m1_dispatch(sh.waves, sh.cgroups, sh.xlds > 0, [&](auto w, auto c, auto xl) {
+      hipLaunchKernelGGL((k_w8a16_m1<decltype(w)::value, decltype(c)::value, decltype(xl)::value>),
+                         grid, block, sh.xlds, st, x, K, q, scale, bias, N, y);
+    });
+    return hipGetLastError();
+  }
   const int64_t rows = 4 * sh.tgroups;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)((M + 15) / 16));
   switch (sh.tgroups) {
@@ -418,6 +550,16 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
 
 hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
                                 const W8A16Shape &sh, hipStream_t st) {
+  if (sh.mblocks == 0) {
+    if (!m1_shape_ok(sh)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)total_blocks), block(64 * sh.waves * sh.cgroups);
+    m1_dispatch(sh.waves, sh.cgroups, sh.xlds > 0, [&](auto w, auto c, auto xl) {
+      hipLaunchKernelGGL(
+          (k_w8a16_m1_grouped<decltype(w)::value, decltype(c)::value, decltype(xl)::value>), grid,
+          block, sh.xlds, st, dev_tab, count);
+    });
+    return hipGetLastError();
+  }
   switch (sh.tgroups) {
     case 1: launch_group_tg<1>(sh.mblocks, sh.waves, total_blocks, st, dev_tab, count); break;
     case 2: launch_group_tg<2>(sh.mblocks, sh.waves, total_blocks, st, dev_tab, count); break;

@@ -49,7 +49,7 @@ INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = "k_w8a16_grouped_smolvlm_decode_sweep_traffic.md"
+TRAFFIC_PROFILE = "k_w8a16_m1_grouped_smolvlm_decode_sweep_traffic.md"
 HEADLINE_SOURCES = ("activation_quantized_linear_amd/csrc/w8a16.hip",
                     "activation_quantized_linear_amd/csrc/common.h")
 
@@ -518,7 +518,7 @@ def main():
             "unit": "GB/s",
             "frac": value / HBM_PEAK_GBS,
             "traffic": traffic_from_profile(TRAFFIC_PROFILE, HEADLINE_SOURCES),
-            "kernel": "k_w8a16_grouped",
+            "kernel": "k_w8a16_m1_grouped",
             "bytes_per_launch": step_bytes,
             "avg_launch_us": ms * 1e3,
             "launches_timed": args.steps,

@@ -199,10 +199,21 @@ def test_group_plan_validation():
     tp = C.c_void_p(buf.ctypes.data)
     f = L.aql_w8a16_group_plan
     assert f(C.cast(_problems(3), C.c_void_p), 3, tp, nb) == aql.AQL_OK
-    hdr = buf[:32].view(np.int32)
-    rows = 4 * hdr[6]  # channels per tile (header: magic, version, count, blocks, waves, mblocks, tgroups)
+    # header: magic, version, count, blocks, waves, mblocks, tgroups, cgroups, xlds
+    hdr = buf[:36].view(np.int32)
+    assert hdr[1] == 2
+    rows = 4 * hdr[6] * hdr[7]  # channels per workgroup
     assert hdr[2] == 3 and hdr[3] == 3 * (-(-32 // rows))  # 3 problems of N = 32, M = 1
     assert hdr[4] in (1, 2, 4, 8) and hdr[5] == 0  # M = 1: the single-row tile
+    assert hdr[7] in (1, 2, 4) and hdr[8] == 1024  # x of K = 64 shared through 1 KiB of LDS
+    # the LDS holding x is sized for the largest K of the group; past 16384 x is not shared
+    assert f(C.cast(_problems(3, {1: dict(K=4096)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
+    assert hdr[8] == 8192
+    assert f(C.cast(_problems(3, {2: dict(K=16400)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
+    assert hdr[8] == 0
+    # M > 1 tiles have one wave tile per workgroup and load x directly
+    assert f(C.cast(_problems(3, {0: dict(M=5)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
+    assert hdr[5] > 0 and hdr[7] == 1 and hdr[8] == 0
     assert f(C.cast(_problems(3), C.c_void_p), 3, tp, nb - 1) == aql.AQL_ERR_WORKSPACE
     assert f(C.cast(_problems(3), C.c_void_p), 0, tp, nb) == aql.AQL_ERR_SHAPE
     assert f(C.cast(_problems(3, {1: dict(K=40)}), C.c_void_p), 3, tp, nb) == aql.AQL_ERR_SHAPE

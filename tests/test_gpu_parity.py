@@ -216,7 +216,9 @@ def test_w8a16_tiny():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 15, 80), (1, 100, 960), (3, 33, 2560),
-                                   (16, 64, 4112), (17, 50, 128), (33, 129, 256), (70, 40, 1024)])
+                                   (16, 64, 4112), (17, 50, 128), (33, 129, 256), (70, 40, 1024),
+                                   (1, 9, 272), (1, 70, 16384), (1, 37, 16400), (1, 200, 20000),
+                                   (1, 4100, 48)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_shapes(M, N, K, with_bias):
     say("w8a16", M, N, K, with_bias)
@@ -412,6 +414,27 @@ def test_w8a16_grouped_mixed():
             yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s),
                                             None if bc is None else bits(bc))
             check_float(host(y.float()), yref, tol, BF16, f"grouped {tuple(y.shape)}")
+
+
+def test_w8a16_grouped_single_row_mixed_k():
+    """A grouped launch of single-row problems whose K differ (x is shared in
+    LDS sized for the largest K) and whose N leave workgroups partly or wholly
+    past the last channel."""
+    g = workloads.gen(710)
+    shapes = [(9, 4112), (2560, 960), (1, 16), (33, 2560), (100, 64), (70, 16384)]
+    probs, refs = [], []
+    for N, K in shapes:
+        w = workloads.small_matrix(g, N, K, std=0.02)
+        x = workloads.small_matrix(g, 1, K).to(torch.bfloat16)
+        q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        y = torch.full((1, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        probs.append((dev(x), q, s, None, y))
+        refs.append(x)
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    aql.aql_linear_w8a16_grouped(host_t, dev_t)
+    for (x, q, s, _, y), xc in zip(probs, refs):
+        yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s), None)
+        check_float(host(y.float()), yref, tol, BF16, f"grouped single-row {tuple(y.shape)}")
 
 
 def test_w8a16_grouped_smolvlm_sweep_in_graph():

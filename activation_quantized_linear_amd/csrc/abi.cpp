@@ -83,8 +83,10 @@ int launched(hipError_t e, const char *fn) {
 
 size_t ws_q8ta(int64_t M, int64_t K) { return 2 * align256((size_t)M * (size_t)K); }
 
+// activation operand (int8 codes, or bf16 differences for the tiled 4-bit
+// kernel: 2 bytes per element), then row scales and zero points
 size_t ws_dq8ca(int64_t M, int64_t K) {
-  return align256((size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
+  return align256(2 * (size_t)M * (size_t)K) + 2 * align256((size_t)M * 4);
 }
 
 // Largest K of the W8A16 kernels: a 16-row tile of x (bf16) stays below the
@@ -187,7 +189,8 @@ int aql_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale, 
   REQUIRE(x && scale && zp, AQL_ERR_NULL, "%s: x, scale and zp must not be NULL", fn);
   if (int e = check_device(fn)) return e;
   return launched(
-      aql::launch_choose_qparams_rows(x, M, K, scale, zp, xq, false, (hipStream_t)stream), fn);
+      aql::launch_choose_qparams_rows(x, M, K, scale, zp, xq, aql::QP_CODES, (hipStream_t)stream),
+      fn);
 }
 
 int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
@@ -401,19 +404,21 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
           fn, need, ws ? ws_bytes : (size_t)0);
   if (int e = check_device(fn)) return e;
   char *base = static_cast<char *>(ws);
+  const size_t xbytes = align256(2 * (size_t)M * (size_t)K);
   int8_t *xq = reinterpret_cast<int8_t *>(base);
-  float *xs = x_scale_out ? x_scale_out
-                          : reinterpret_cast<float *>(base + align256((size_t)M * (size_t)K));
+  float *xs = x_scale_out ? x_scale_out : reinterpret_cast<float *>(base + xbytes);
   int32_t *xz = x_zp_out ? x_zp_out
-                         : reinterpret_cast<int32_t *>(base + align256((size_t)M * (size_t)K) +
-                                                       align256((size_t)M * 4));
+                         : reinterpret_cast<int32_t *>(base + xbytes + align256((size_t)M * 4));
   hipStream_t st = (hipStream_t)stream;
   const bool q4 = wfmt == AQL_W_Q4GSW;
-  hipError_t e = aql::launch_choose_qparams_rows(x, M, K, xs, xz, xq, q4, st);
+  const aql::QpOut mode = !q4 ? aql::QP_CODES
+                              : (M <= aql::kQ4StreamMaxM ? aql::QP_CODES_PERM8 : aql::QP_DIFF_BF16);
+  hipError_t e = aql::launch_choose_qparams_rows(x, M, K, xs, xz, xq, mode, st);
   if (e != hipSuccess) return launched(e, fn);
   if (q4) {
     aql::Q4Args a{};
     a.xq = xq;
+    a.xd = reinterpret_cast<const uint16_t *>(xq);
     a.xs = xs;
     a.xz = xz;
     a.q4 = static_cast<const uint8_t *>(wq);

@@ -32,11 +32,14 @@ hipError_t launch_quantize_weight_q4gsw(const float *w, int64_t N, int64_t K, ui
 hipError_t launch_quantize_act_per_tensor(const float *x, int64_t count, float s1, int32_t z1,
                                           bool two_pass, float s2, int32_t z2, int8_t *xq1,
                                           int8_t *xq2, hipStream_t st);
-// Per-row qparams; xq (may be null) is written in natural k order, or, with
-// permute8, with every 8-k block stored as k = 0,2,4,6,1,3,5,7 (the order the
-// 4-bit GEMM unpacks its weights in).
+// Per-row qparams; the activation output (may be null) is, by mode: int8 codes
+// xq in natural k order; int8 codes with every 8-k block stored as
+// k = 0,2,4,6,1,3,5,7 (the order the streaming 4-bit kernel unpacks its weights
+// in); or bf16 differences xq - zp (integers in [-255, 255], exact in bf16) in
+// natural k order, the operand of the tiled 4-bit kernel.
+enum QpOut { QP_CODES = 0, QP_CODES_PERM8 = 1, QP_DIFF_BF16 = 2 };
 hipError_t launch_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale,
-                                      int32_t *zp, int8_t *xq, bool permute8, hipStream_t st);
+                                      int32_t *zp, void *out, QpOut mode, hipStream_t st);
 
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
@@ -101,10 +104,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_i8(const GemmArgs &a, GemmEpi epi, bool two_pass, hipStream_t st);
 
-// 4-bit group-32 weights, dynamic per-row activations: xq must be in the
-// permute8 order (see launch_choose_qparams_rows).
+// 4-bit group-32 weights, dynamic per-row activations. M <= kQ4StreamMaxM reads
+// xq in the permute8 order, larger M the bf16 differences xd (see
+// launch_choose_qparams_rows).
+constexpr int64_t kQ4StreamMaxM = 16;
 struct Q4Args {
-  const int8_t *xq;     // [M, K] int8, permute8 order
+  const int8_t *xq;     // [M, K] int8, permute8 order (M <= 16)
+  const uint16_t *xd;   // [M, K] bf16 xq - zp, natural order (M > 16)
   const float *xs;      // [M]
   const int32_t *xz;    // [M]
   const uint8_t *q4;    // [N, K/2] packed nibbles

@@ -198,194 +198,204 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
 }
 
 // ----------------------------------------------------------------- tiled
-// M > 16. The per-group fold (one 24-bit multiply-add for the zero point, one
-// convert, one fused multiply-add with the group scale per output and group)
-// runs on the vector ALU and bounds the kernel; everything else is arranged
-// around keeping it fed. A 64 x 64 output tile per workgroup; each wave owns a
-// 32 x 32 block (2 x 2 MFMA tiles, fp32 accumulators in registers) and, with
-// KH = 2, every other group of each 128-k stage (the halves are summed once
-// at the end). One v_mfma_i32_16x16x32_i8 is exactly one group.
+// M > 16, on the bf16 matrix cores with exact integer arithmetic. The
+// activation operand is d = xq - zp as bf16 (an integer in [-255, 255], exact),
+// written by the qparams kernel with each 8-k block in the order the weights
+// unpack in; a weight nibble c becomes the bf16 128 + (c + 8) by OR-ing it into
+// the mantissa of 128 (also exact). Per 32-k group
+// one MFMA with a constant -136 operand gives -136 sum_k d per row, and the
+// group's MFMA, accumulating on top of it, gives
+//     sum_k d (136 + c) - 136 sum_k d = sum_k (xq - zp) c
+// exactly: every product and partial sum is an integer below 2^24, so fp32
+// accumulation does not round. The zero point therefore costs no vector op,
+// and the per-output, per-group work is one FMA with the group scale (the
+// integer path needs a multiply-add for the zero point, a convert and the FMA).
+// The correction is per row, so it is formed once per row tile and used as the
+// accumulator input of every column tile's MFMA.
 //
-// Operands go global -> LDS by buffer loads that write LDS, per 128-k stage:
-// xq 64 rows x 128 B (8 instructions), nibbles 64 rows x 64 B (4), group
-// scales and group sums 64 rows x 16 B (4 dword instructions each) and four
-// zero-filling loads into a scratch slot so every wave issues the same count
-// (24 / waves). A
-// 4-stage ring keeps three stages in flight behind exact vmcnt waits and a
-// fence-free barrier, as in the int8 GEMM. xq rows store their 16-byte
-// chunks XOR-swizzled by row mod 8, nibble rows by row mod 4.
-namespace {
-constexpr int TB = 64;                          // tile rows and columns
-constexpr int Q_STAGES = 3;
-constexpr int QA_BYTES = TB * 128;              // xq: 128 k
-constexpr int QB_BYTES = TB * 64;               // nibbles: 128 k
-constexpr int QG_BYTES = TB * 16;               // 4 group scales (or sums) per row
-constexpr int Q_STAGE = QA_BYTES + QB_BYTES + 2 * QG_BYTES;  // 14 KB
-constexpr int Q_DUMMY = Q_STAGES * Q_STAGE;     // scratch slot for padding loads
-constexpr int Q_LDS = Q_DUMMY + 1024;
-constexpr int Q_TILE_LD = TB + 4;               // words per staged output row
-static_assert(TB * Q_TILE_LD * 4 + 4 * 4 * 64 * 16 <= Q_DUMMY, "epilogue (tile + half-sum exchange) fits in the ring");
-}  // namespace
+// Tile: WM x WN waves of (16 TI) x (16 TJ) outputs, times KH waves taking
+// alternate groups of each 64-k stage (their sums meet in LDS at the end).
+// Operands go global -> LDS by buffer loads that write LDS (bf16 d rows of
+// 128 B with 16-byte chunks XOR-swizzled by (row / 2) mod 8; nibble rows of
+// 32 B with their two group chunks swapped on odd eighths of rows; 16 bytes of
+// group scales per row, of which the stage uses the first two) into a ring,
+// with exact vmcnt waits and a fence-free barrier as in the int8 GEMM. Every
+// wave issues the same number of loads per stage; the spare ones zero-fill a
+// scratch slot. The output tile is staged in LDS per wave and written as
+// whole rows.
+template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_>
+struct QT {
+  static constexpr int TI = TI_, TJ = TJ_, WM = WM_, WN = WN_, KH = KH_, STAGES = STAGES_;
+  static constexpr int NW = WM * WN * KH;
+  static constexpr int BM = 16 * TI * WM, BN = 16 * TJ * WN;
+  // loads per stage of each kind, rounded up to a multiple of the wave count
+  // so that a wave's q-th load is of one kind on every wave (the extra loads
+  // fetch rows past the tile: the range check makes them zero, and their LDS
+  // rows are never read)
+  static constexpr int QA = (BM * 128 / 1024 + NW - 1) / NW;  // bf16 d: 8 rows x 128 B each
+  static constexpr int QB = (BN * 32 / 1024 + NW - 1) / NW;   // nibbles: 32 rows x 32 B
+  static constexpr int QG = (BN * 16 / 1024 + NW - 1) / NW;   // scales: 64 rows x 16 B
+  static constexpr int NL = QA + QB + QG;
+  static constexpr int A_BYTES = QA * NW * 1024, B_BYTES = QB * NW * 1024, G_BYTES = QG * NW * 1024;
+  static constexpr int B_OFF = A_BYTES, G_OFF = A_BYTES + B_BYTES;
+  static constexpr int STAGE = A_BYTES + B_BYTES + G_BYTES;
+  static constexpr int RING = STAGES * STAGE;
+  static constexpr int OUT_LD = 16 * TJ + 4;  // words per staged output row
+  static constexpr int OUT_WAVE = 16 * TI * OUT_LD * 4;
+  static constexpr int XCH = KH == 2 ? WM * WN * 64 * TI * TJ * 16 : 0;  // partial sums of kh = 1
+  static constexpr int EPI = XCH + WM * WN * OUT_WAVE;
+  static constexpr int LDS = RING > EPI ? RING : EPI;
+};
+using QTL = QT<4, 4, 2, 2, 1, 3>;  // 128 x 128, large M
+using QTS = QT<4, 2, 1, 2, 2, 4>;  // 64 x 64, groups split over two waves
 
-// Kind of a wave's q-th load per stage (see the kernel): xq, nibbles,
-// padding or a group-scale / group-sum dword load.
-enum { KXQ, KNIB, KPAD, KGS };
-template <int KH>
-__host__ __device__ constexpr int q4_load_kind(int q) {
-  return KH == 1 ? (q < 2 ? KXQ : q == 2 ? KNIB : q == 3 ? KPAD : KGS)
-                 : (q == 0 ? KXQ : q == 1 ? KNIB : KGS);
+__device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t d = bits | (bits << 16);
+  return __builtin_bit_cast(bf16x8, u32x4{d, d, d, d});
 }
 
-template <int KH>
-__global__ __launch_bounds__(256 * KH, 2 / KH) void k_dq8ca_q4_tiled(Q4Args p, int tiles_m, int tiles_n) {
+// 8 nibbles of one lane (k = 0..7 of its 8-k slice, k even in the low nibble
+// of each byte) -> bf16 136 + c in the order k = 0,4,1,5,2,6,3,7: dword i holds
+// nibbles i and i + 4, which one shift and one mask-or pull out together.
+__device__ __forceinline__ bf16x8 nib_bf16x8(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = ((u >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_>
+__global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Args p, int tiles_m,
+                                                                            int tiles_n) {
+  using C = QT<TI_, TJ_, WM_, WN_, KH_, STAGES_>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int NW = 4 * KH, NL = 24 / NW;  // waves, loads per wave per stage
+  constexpr int TI = C::TI, TJ = C::TJ, KH = C::KH, NL = C::NL, STAGES = C::STAGES;
   const int nt = tiles_m * tiles_n;
   const int lin = blockIdx.x;
   int tile = lin;
   if ((nt & 7) == 0) tile = (lin & 7) * (nt >> 3) + (lin >> 3);
   const int tn = tile / tiles_m, tm = tile % tiles_m;
-  const int64_t n0 = (int64_t)tn * TB, m0 = (int64_t)tm * TB;
+  const int64_t n0 = (int64_t)tn * C::BN, m0 = (int64_t)tm * C::BM;
   const int64_t M = p.M, N = p.N, K = p.K, G = K / 32, KB = K / 2;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+  // wave = (kh * WM + wm) * WN + wn
+  const int wn = wave % C::WN, wm = (wave / C::WN) % C::WM, kh = wave / (C::WN * C::WM);
   const int r = lane & 15, g4 = lane >> 4;
-  const int64_t mval = M - m0 < TB ? M - m0 : TB;
-  const int64_t nval = N - n0 < TB ? N - n0 : TB;
+  const int64_t mval = M - m0 < C::BM ? M - m0 : C::BM;
+  const int64_t nval = N - n0 < C::BN ? N - n0 : C::BN;
 
-  // ---- per stage 24 loads, NL per wave. Load q of a wave is of one kind for
-  // every wave (so its size is a compile-time constant); waves differ only in
-  // uniform addresses. Kinds: xq (8 rows x 128 B), nibbles (16 rows x 64 B),
-  // group scales / group sums (16 rows x 4 dwords, one dword per lane so each is
-  // range-checked on its own: a row's groups need not fill the last stage),
-  // and zero-filling padding into a scratch slot.
-  // (buffer descriptors are formed at issue time: an array of them is not a
-  // host-side type)
-  const void *rbase[NL];
-  uint32_t rbytes[NL];
-  uint32_t off[NL], lds_off[NL], kstep[NL];
-  int kin_lim[NL];  // per lane: first stage whose bytes for this lane lie past K
+  // ---- loads: the q-th load of wave w is number l = (q - first q of its
+  // kind) * NW + w of that kind: bf16 d (8 rows x 128 B), nibbles (32 rows x
+  // 32 B), group scales (64 rows x 16 B). The kind of each q is a compile-time
+  // constant, so its descriptor is uniform by construction.
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.xd + m0 * K, (uint32_t)(mval * K * 2));
+  const __amdgpu_buffer_rsrc_t rb = rsrc(p.q4 + n0 * KB, (uint32_t)(nval * KB));
+  const __amdgpu_buffer_rsrc_t rg = rsrc(p.gs + n0 * G, (uint32_t)(nval * G * 4));
+  uint32_t off[NL], lds_off[NL];
+  int klim[NL];  // first stage whose bytes for this lane lie past the row
 #pragma unroll
   for (int q = 0; q < NL; ++q) {
-    const int kind = q4_load_kind<KH>(q);
-    if (kind == KXQ) {
-      const int slot = KH == 1 ? 4 * q + wave : wave;  // 0..7
-      const int row = 8 * slot + (lane >> 3), c = (lane & 7) ^ (row & 7);
-      rbase[q] = p.xq + m0 * K;
-      rbytes[q] = (uint32_t)(mval * K);
-      off[q] = (uint32_t)row * (uint32_t)K + 16u * c;
-      lds_off[q] = (uint32_t)(slot * 1024);
-      kstep[q] = 128;
-      kin_lim[q] = (int)((K - 16 * c + 127) / 128);
-    } else if (kind == KNIB || kind == KPAD) {
-      // KH = 2: waves 4..7 pad
-      const bool pad = kind == KPAD || wave >= 4;
-      const int slot = wave & 3;
-      const int row = 16 * slot + (lane >> 2), c = (lane & 3) ^ (row & 3);
-      rbase[q] = p.q4 + n0 * KB;
-      rbytes[q] = pad ? 0u : (uint32_t)(nval * KB);
-      off[q] = pad ? (uint32_t)OOB : (uint32_t)row * (uint32_t)KB + 16u * c;
-      lds_off[q] = pad ? (uint32_t)Q_DUMMY : (uint32_t)(QA_BYTES + slot * 1024);
-      kstep[q] = pad ? 0u : 64u;
-      kin_lim[q] = pad ? 0 : (int)((KB - 16 * c + 63) / 64);
+    if (q < C::QA) {
+      const int l = q * C::NW + wave;
+      const int row = 8 * l + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
+      off[q] = (uint32_t)row * (uint32_t)(2 * K) + 16u * c;
+      lds_off[q] = (uint32_t)(l * 1024);
+      klim[q] = (int)((2 * K - 16 * c + 127) / 128);
+    } else if (q < C::QA + C::QB) {
+      const int l = (q - C::QA) * C::NW + wave;
+      const int row = 32 * l + (lane >> 1), c = (lane & 1) ^ ((row >> 3) & 1);
+      off[q] = (uint32_t)row * (uint32_t)KB + 16u * c;
+      lds_off[q] = (uint32_t)(C::B_OFF + l * 1024);
+      klim[q] = (int)((KB - 16 * c + 31) / 32);
     } else {
-      // KH = 1: load 4 = scales, 5 = sums; KH = 2: waves 0..3 scales, 4..7 sums
-      const bool sums = KH == 1 ? q == 5 : wave >= 4;
-      const int part = wave & 3;
-      const int row = 16 * part + (lane >> 2), e = lane & 3;
-      rbase[q] = sums ? (const void *)(p.gsum + n0 * G) : (const void *)(p.gs + n0 * G);
-      rbytes[q] = (uint32_t)(nval * G * 4);
-      off[q] = (uint32_t)row * (uint32_t)(G * 4) + 4u * e;
-      lds_off[q] = (uint32_t)(QA_BYTES + QB_BYTES + (sums ? QG_BYTES : 0) + part * 256);
-      kstep[q] = 16;
-      kin_lim[q] = (int)((G - e + 3) / 4);
+      const int l = (q - C::QA - C::QB) * C::NW + wave;
+      const int row = 64 * l + lane;
+      off[q] = (uint32_t)row * (uint32_t)(G * 4);
+      lds_off[q] = (uint32_t)(C::G_OFF + l * 1024);
+      klim[q] = (int)((G + 1) / 2);
     }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   auto issue = [&](int kt) {
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const bool pad = lds_off[q] == (uint32_t)Q_DUMMY;
-      const uint32_t dst = lds_base + lds_off[q] + (pad ? 0u : (uint32_t)((kt % Q_STAGES) * Q_STAGE));
-      const int o = kt < kin_lim[q] ? (int)(off[q] + kstep[q] * (uint32_t)kt) : OOB;
+      const uint32_t kstep = q < C::QA ? 128u : (q < C::QA + C::QB ? 32u : 8u);
+      const uint32_t dst = lds_base + lds_off[q] + (uint32_t)((kt % STAGES) * C::STAGE);
+      const int o = kt < klim[q] ? (int)(off[q] + kstep * (uint32_t)kt) : OOB;
       lds_void *d = (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst);
-      const __amdgpu_buffer_rsrc_t rs = rsrc(rbase[q], rbytes[q]);
-      if (q4_load_kind<KH>(q) == KGS)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 4, o, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, o, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t rs = q < C::QA ? ra : (q < C::QA + C::QB ? rb : rg);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, o, 0, 0, 0);
     }
   };
 
-  int zp16[2][4];
+  f32x4 f[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + wm * 32 + i * 16 + 4 * g4 + v;
-      zp16[i][v] = m < M ? -16 * p.xz[m] : 0;
-    }
-  f32x4 f[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) f[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+    for (int j = 0; j < TJ; ++j) f[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int kt) {
-    const char *st = smem + (kt % Q_STAGES) * Q_STAGE;
+    const char *st = smem + (kt % STAGES) * C::STAGE;
+    const bf16x8 bneg = bf16x8_splat(0xC308u);  // -136 in every element
 #pragma unroll
-    for (int x = 0; x < 4 / KH; ++x) {
+    for (int x = 0; x < 2 / KH; ++x) {
       const int gg = kh + KH * x;  // group within the stage
-      if (4 * kt + gg < G) {       // uniform: the last stage may hold fewer groups
-        long fa[2], fb[2];
-        float gsv[2];
-        int gmv[2];
+      if (2 * kt + gg < G) {       // uniform: the last stage may hold one group
+        bf16x8 a[TI], b[TJ];
+        f32x4 corr[TI];
+        float gsv[TJ];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int R = wm * 32 + i * 16 + r;
-          const int c = 2 * gg + (g4 >> 1);
-          fa[i] = *reinterpret_cast<const long *>(st + R * 128 + 16 * (c ^ (R & 7)) + 8 * (g4 & 1));
+        for (int i = 0; i < TI; ++i) {
+          const int R = wm * 16 * TI + 16 * i + r;
+          const int c = 4 * gg + g4;
+          a[i] = *reinterpret_cast<const bf16x8 *>(st + R * 128 + 16 * (c ^ ((R >> 1) & 7)));
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int R = wn * 32 + j * 16 + r;
-          const uint32_t w = *reinterpret_cast<const uint32_t *>(st + QA_BYTES + R * 64 +
-                                                                 16 * (gg ^ (R & 3)) + 4 * g4);
-          fb[j] = unpack_q4x8(w);
-          gsv[j] = *reinterpret_cast<const float *>(st + QA_BYTES + QB_BYTES + R * 16 + 4 * gg);
-          gmv[j] = *reinterpret_cast<const int *>(st + QA_BYTES + QB_BYTES + QG_BYTES + R * 16 + 4 * gg);
+        for (int j = 0; j < TJ; ++j) {
+          const int R = wn * 16 * TJ + 16 * j + r;
+          const uint32_t w = *reinterpret_cast<const uint32_t *>(
+              st + C::B_OFF + R * 32 + 16 * (gg ^ ((R >> 3) & 1)) + 4 * g4);
+          b[j] = nib_bf16x8(w);
+          gsv[j] = *reinterpret_cast<const float *>(st + C::G_OFF + R * 16 + 4 * gg);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TI; ++i)
+          corr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bneg, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const i32x4 t = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[i], fb[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)  // |zp16| <= 2048, |gsum| <= 256: 24-bit product
-              f[i][j][v] += gsv[j] * (float)(t[v] + __mul24(zp16[i][v], gmv[j]));
+          for (int j = 0; j < TJ; ++j) {
+            const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], corr[i], 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) f[i][j][v] = __builtin_fmaf(gsv[j], t[v], f[i][j][v]);
           }
       }
     }
   };
 
-  const int nk = (int)((K + 127) / 128);
+  const int nk = (int)((K + 63) / 64);
 #pragma unroll
-  for (int s = 0; s < Q_STAGES - 1; ++s) issue(s);
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
   int kt = 0;
-  for (; kt < nk - (Q_STAGES - 1); ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (Q_STAGES - 2)));
+  static_assert(NL * (STAGES - 2) < 16, "vmcnt immediate");
+  for (; kt < nk - (STAGES - 1); ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
     __builtin_amdgcn_s_barrier();
-    issue(kt + Q_STAGES - 1);
+    issue(kt + STAGES - 1);
     compute(kt);
     __builtin_amdgcn_s_waitcnt(0xC07F);
   }
 #pragma unroll
-  for (int t = 0; t < Q_STAGES - 1; ++t) {
+  for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {
-      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (Q_STAGES - 2)));
-      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (Q_STAGES - 3)));
+      // stages issued after stage kt: STAGES - 2 - t
+      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
+      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (STAGES > 3 ? NL * (STAGES - 3) : 0));
+      else if (t == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (STAGES > 4 ? NL * (STAGES - 4) : 0));
       else __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       compute(kt);
@@ -394,47 +404,65 @@ __global__ __launch_bounds__(256 * KH, 2 / KH) void k_dq8ca_q4_tiled(Q4Args p, i
     ++kt;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  __syncthreads();  // ring no longer read or written
 
-  // ---- sum the group halves (KH = 2), then stage the tile in LDS
-  f32x4 *xch = reinterpret_cast<f32x4 *>(smem + TB * Q_TILE_LD * 4);
+  // ---- KH = 2: waves kh = 1 hand their sums to kh = 0
+  const int pw = wm * C::WN + wn;  // plane wave 0 .. WM WN - 1
   if constexpr (KH == 2) {
+    f32x4 *xch = reinterpret_cast<f32x4 *>(smem);
     if (kh == 1) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) xch[((wave - 4) * 4 + i * 2 + j) * 64 + lane] = f[i][j];
+        for (int j = 0; j < TJ; ++j) xch[((pw * TI + i) * TJ + j) * 64 + lane] = f[i][j];
     }
     __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) f[i][j] += xch[((pw * TI + i) * TJ + j) * 64 + lane];
+    }
   }
-  float *tl = reinterpret_cast<float *>(smem);
-  if (kh == 0) {
+  if (kh != 0) return;
+
+  // ---- y = xs[m] f + bias[n], staged per wave: f[i][j] lane holds rows
+  // 4 g4 + v, column r of MFMA tile (i, j)
+  float *tl = reinterpret_cast<float *>(smem + C::XCH + pw * C::OUT_WAVE);
+  const int64_t wm0 = m0 + wm * 16 * TI, wn0 = n0 + wn * 16 * TJ;
+  // row scales and bias by range-checked loads, all in flight together (rows
+  // past M and columns past N, or no bias, read 0)
+  const __amdgpu_buffer_rsrc_t rxs = rsrc(p.xs + m0, (uint32_t)(mval * 4));
+  const __amdgpu_buffer_rsrc_t rbi = rsrc(p.bias ? p.bias + n0 : p.xs, p.bias ? (uint32_t)(nval * 4) : 0u);
+  float xsv[TI][4], bv[TJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x4 v4 = f[i][j];
-        if constexpr (KH == 2) v4 += xch[(wave * 4 + i * 2 + j) * 64 + lane];
-        const int col = wn * 32 + j * 16 + r;
-        const int64_t n = n0 + col;
-        const float bv = (n < N && p.bias) ? p.bias[n] : 0.0f;
+    for (int v = 0; v < 4; ++v)
+      xsv[i][v] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rxs, 4 * (wm * 16 * TI + 16 * i + 4 * g4 + v), 0, 0));
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = wm * 32 + i * 16 + 4 * g4 + v;
-          const int64_t m = m0 + row;
-          const float xs = m < M ? p.xs[m] : 0.0f;
-          tl[row * Q_TILE_LD + col] = xs * (v4[v] * 0.0625f) + bv;
-        }
-      }
-  }
-  __syncthreads();
-  // 16 lanes x 16 B per row
+  for (int j = 0; j < TJ; ++j)
+    bv[j] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rbi, 4 * (wn * 16 * TJ + 16 * j + r), 0, 0));
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tl[(16 * i + 4 * g4 + v) * C::OUT_LD + 16 * j + r] = xsv[i][v] * f[i][j][v] + bv[j];
+  // the wave reads back only what it wrote: no barrier needed beyond the
+  // wave's own LDS ordering
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  constexpr int CPR = 4 * TJ;  // 16-byte chunks per row
   const bool vec = (N & 3) == 0;
-  for (int u = tid; u < TB * 16; u += 256 * KH) {
-    const int row = u >> 4, c = u & 15;
-    const int64_t m = m0 + row, n = n0 + 4 * c;
+#pragma unroll
+  for (int u = lane; u < 16 * TI * CPR; u += 64) {
+    const int row = u / CPR, c = u % CPR;
+    const int64_t m = wm0 + row, n = wn0 + 4 * c;
     if (m >= M || n >= N) continue;
-    const f32x4 val = *reinterpret_cast<const f32x4 *>(tl + row * Q_TILE_LD + 4 * c);
+    const f32x4 val = *reinterpret_cast<const f32x4 *>(tl + row * C::OUT_LD + 4 * c);
     float *dst = p.y + m * N + n;
     if (vec) {
       *reinterpret_cast<f32x4 *>(dst) = val;
@@ -466,10 +494,28 @@ void launch_stream_tg(int MB, int W, dim3 grid, const Q4Args &a, hipStream_t st)
   }
 }
 
+template <typename C>
+void launch_tiled(const Q4Args &a, hipStream_t st) {
+  constexpr auto kern = k_dq8ca_q4_tiled<C::TI, C::TJ, C::WM, C::WN, C::KH, C::STAGES>;
+  const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
+  const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
+  // more than 64 KB of dynamic LDS: raise the function's limit once (a launch
+  // the limit does not allow reports its own error)
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)kern,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * C::NW),
+                     C::LDS, st, a, tiles_m, tiles_n);
+}
+
 }  // namespace
 
 hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
-  if (a.M <= 16) {
+  if (a.M <= kQ4StreamMaxM) {
     // same launch-shape rule as the weight-only GEMV: 8-channel tiles for
     // M <= 2, 16 otherwise; waves per workgroup until ~768 wave-tiles
     const int MB = a.M <= 4 ? 1 : (a.M <= 8 ? 2 : 4);
@@ -482,32 +528,11 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
-    const int tiles_m = (int)((a.M + TB - 1) / TB);
-    const int tiles_n = (int)((a.N + TB - 1) / TB);
-    const int64_t tiles = (int64_t)tiles_m * tiles_n;
-    // split each stage's groups over two waves when there are too few tiles
-    // to give every SIMD several waves
-    if (tiles < 1024) {
-      static bool attr2 = false;
-      if (!attr2) {
-        (void)hipFuncSetAttribute((const void *)k_dq8ca_q4_tiled<2>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, Q_LDS);
-        (void)hipGetLastError();
-        attr2 = true;
-      }
-      hipLaunchKernelGGL(k_dq8ca_q4_tiled<2>, dim3((unsigned)tiles), dim3(512), Q_LDS, st, a,
-                         tiles_m, tiles_n);
-    } else {
-      static bool attr1 = false;
-      if (!attr1) {
-        (void)hipFuncSetAttribute((const void *)k_dq8ca_q4_tiled<1>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, Q_LDS);
-        (void)hipGetLastError();
-        attr1 = true;
-      }
-      hipLaunchKernelGGL(k_dq8ca_q4_tiled<1>, dim3((unsigned)tiles), dim3(256), Q_LDS, st, a,
-                         tiles_m, tiles_n);
-    }
+    // 128 x 128 tiles once they give every CU a few; else 64 x 64 tiles with
+    // the groups split over two waves
+    const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
+    if (tl >= 512) launch_tiled<QTL>(a, st);
+    else launch_tiled<QTS>(a, st);
   }
   return hipGetLastError();
 }

@@ -232,10 +232,10 @@ __global__ __launch_bounds__(256) void k_quantize_act_per_tensor(
 // ExecuTorch 8da4w choose_qparams_affine, read as the affine min/max rule:
 // mn = min(min x, 0), mx = max(max x, 0), s = max((mx - mn) / 255, eps),
 // zp = clamp(-128 - rint(mn / s)), then xq = clamp(rint(x * (1/s)) + zp).
-template <int TPR, int VPT, bool PERM>
+template <int TPR, int VPT, int MODE>
 __global__ __launch_bounds__(256) void k_choose_qparams_rows(
     const float *__restrict__ x, int64_t M, int64_t K, float *__restrict__ scale,
-    int32_t *__restrict__ zp, int8_t *__restrict__ xq) {
+    int32_t *__restrict__ zp, void *__restrict__ xq) {
   __shared__ float red_f[4];
   constexpr int RPW = 256 / TPR;
   const int t = threadIdx.x % TPR;
@@ -274,12 +274,27 @@ __global__ __launch_bounds__(256) void k_choose_qparams_rows(
   }
   if (xq == nullptr || !active) return;
   const float inv = 1.0f / s;
-  int8_t *out = xq + base;
+  int8_t *out = static_cast<int8_t *>(xq) + base;
   auto emit = [&](int64_t j, float4 u) {
     const int a = (int)act_code(u.x, inv, zf), b = (int)act_code(u.y, inv, zf);
     const int c = (int)act_code(u.z, inv, zf), d = (int)act_code(u.w, inv, zf);
-    if constexpr (!PERM) {
+    if constexpr (MODE == QP_CODES) {
       reinterpret_cast<uint32_t *>(out)[j] = pack4(a, b, c, d);
+    } else if constexpr (MODE == QP_DIFF_BF16) {
+      // xq - zp is an integer of at most 9 bits: its float's top half is the
+      // exact bf16. Each 8-k block is stored as k = 0,4,1,5,2,6,3,7 (the order
+      // the tiled 4-bit kernel unpacks nibbles in): the lanes holding k0..k3
+      // (even j) and k4..k7 (odd j, the next lane) swap two values each, then
+      // the even lane writes k0,k4,k1,k5 and the odd lane k2,k6,k3,k7. Both
+      // lanes of a pair are always active: rows hold a multiple of 8 codes.
+      const int z = (int)zf;
+      const uint32_t ba = __float_as_uint((float)(a - z)) >> 16, bb = __float_as_uint((float)(b - z)) >> 16;
+      const uint32_t bc = __float_as_uint((float)(c - z)) >> 16, bd = __float_as_uint((float)(d - z)) >> 16;
+      const bool odd = (j & 1) != 0;
+      const uint32_t got = (uint32_t)__shfl_xor((int)(odd ? (ba | (bb << 16)) : (bc | (bd << 16))), 1);
+      const uint32_t w0 = odd ? ((got & 0xffffu) | (bc << 16)) : (ba | (got << 16));
+      const uint32_t w1 = odd ? ((got >> 16) | (bd << 16)) : (bb | (got & 0xffff0000u));
+      reinterpret_cast<uint2 *>(static_cast<uint16_t *>(xq) + base)[j] = make_uint2(w0, w1);
     } else {
       // 8-k block stored as k = 0,2,4,6,1,3,5,7: the even half of the vector
       // (k0..k3) fills bytes (0,1) and (4,5); the odd half (k4..k7) bytes (2,3), (6,7).
@@ -301,9 +316,9 @@ __global__ __launch_bounds__(256) void k_choose_qparams_rows(
   }
 }
 
-template <bool PERM>
+template <int PERM>
 hipError_t cq_dispatch(const float *x, int64_t M, int64_t K, float *scale, int32_t *zp,
-                       int8_t *xq, hipStream_t st) {
+                       void *xq, hipStream_t st) {
   const int64_t nvec = K / 4;
   if (nvec <= 64 * 4) {
     const dim3 grid((unsigned)((M + 3) / 4));
@@ -378,9 +393,13 @@ hipError_t launch_quantize_act_per_tensor(const float *x, int64_t count, float s
 }
 
 hipError_t launch_choose_qparams_rows(const float *x, int64_t M, int64_t K, float *scale,
-                                      int32_t *zp, int8_t *xq, bool permute8, hipStream_t st) {
-  return permute8 ? cq_dispatch<true>(x, M, K, scale, zp, xq, st)
-                  : cq_dispatch<false>(x, M, K, scale, zp, xq, st);
+                                      int32_t *zp, void *out, QpOut mode, hipStream_t st) {
+  switch (mode) {
+    case QP_CODES: return cq_dispatch<QP_CODES>(x, M, K, scale, zp, out, st);
+    case QP_CODES_PERM8: return cq_dispatch<QP_CODES_PERM8>(x, M, K, scale, zp, out, st);
+    case QP_DIFF_BF16: return cq_dispatch<QP_DIFF_BF16>(x, M, K, scale, zp, out, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace aql

@@ -365,6 +365,22 @@ def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
     check_float(y, o["y"], o["tol"], FP32, f"dq8ca {wfmt} {M}x{N}x{K}")
 
 
+def test_dq8ca_q4_large_tiles_ragged():
+    """Enough rows and columns for the 128 x 128 tiles of the 4-bit kernel, with
+    ragged edges in M and N and an odd number of groups (the last 64-k stage
+    holds one group)."""
+    M, N, K = 2000, 4100, 96
+    say("dq8ca q4 large ragged", M, N, K)
+    g = workloads.gen(650)
+    x = _edge_rows(workloads.small_matrix(g, M, K))
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    b = workloads.small_matrix(g, 1, N)[0]
+    y, wq, wsc, xs, xz, group = _dq8ca_case(x, w, aql.AQL_W_Q4GSW, b)
+    o = oracle.linear_dq8ca(x.numpy(), wq, wsc, aql.AQL_W_Q4GSW, group, b.numpy())
+    assert np.array_equal(xs, o["x_scale"]) and np.array_equal(xz, o["x_zp"])
+    check_float(y, o["y"], o["tol"], FP32, f"dq8ca q4 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M", list(workloads.DYN_MS))
 def test_dq8ca_8da4w_full_size(M):
     d = workloads.dyn8da4w(M, seed=4)

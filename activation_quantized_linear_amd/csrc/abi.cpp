@@ -11,7 +11,10 @@
 #include <string>
 
 #include "aql.h"
-#include "common.h"
+#include "dq8ca_q4.h"
+#include "gemm_i8.h"
+#include "quant.h"
+#include "w8a16.h"
 #include "measure.h"
 #include "w8a16_gemm.h"
 

@@ -16,7 +16,7 @@
 //
 // Either way every 32-k group's int32 sum is formed exactly by the matrix cores
 // and folded into the fp32 accumulator with its group scale right away.
-#include "common.h"
+#include "dq8ca_q4.h"
 
 namespace aql {
 namespace {

@@ -30,7 +30,7 @@
 // Epilogue: the output tile is assembled in LDS (row stride 132 words, bank-
 // conflict free for the MFMA output layout) and written with 16-byte stores of
 // whole rows.
-#include "common.h"
+#include "gemm_i8.h"
 
 namespace aql {
 namespace {

@@ -4,7 +4,7 @@
 // float input, one write of the codes; a row that has to be reduced first
 // (absmax, min/max) is held in registers between the reduction and the
 // quantization so it is read from HBM once.
-#include "common.h"
+#include "quant.h"
 
 #include <float.h>
 

@@ -27,7 +27,7 @@
 // are laid end to end in one grid and found through a device table.
 #include <type_traits>
 
-#include "common.h"
+#include "w8a16.h"
 
 namespace aql {
 namespace {

@@ -51,6 +51,7 @@ MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = "k_w8a16_m1_grouped_smolvlm_decode_sweep_traffic.md"
 HEADLINE_SOURCES = ("activation_quantized_linear_amd/csrc/w8a16.hip",
+                    "activation_quantized_linear_amd/csrc/w8a16.h",
                     "activation_quantized_linear_amd/csrc/common.h")
 
 
@@ -397,21 +398,29 @@ def sec_copy(torch, aql, workloads, dev, mib=256, reps=20):
 def ceilings(torch, aql, dev):
     """Attainable ceilings on this GPU, measured in the same run: a read-only
     HBM stream (two 512 MiB buffers rotated, so no read hits the 256 MB
-    Infinity Cache) and back-to-back int8 MFMAs on all CUs."""
+    Infinity Cache), the same stream in launches of one 7B weight matrix
+    (56 MiB = 14336 x 4096 int8, ten buffers rotated), and back-to-back int8
+    MFMAs on all CUs."""
     n = 512 << 20
     bufs = [torch.full((n,), 1, dtype=torch.uint8, device=dev) for _ in range(2)]
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     rd_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_read(bufs[i], sink), 10, 2)
     del bufs
+    n7 = 56 << 20
+    bufs = [torch.full((n7,), 1, dtype=torch.uint8, device=dev) for _ in range(10)]
+    rd7_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_read(bufs[i], sink), 50, 10)
+    del bufs
+    rd7 = n7 / (rd7_ms * 1e-3) / 1e9
     iters = 20000
     ops = 2048 * 32768 * 16 * iters
     mf_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_mfma_i8(iters, sink), 3, 1)
     rd = n / (rd_ms * 1e-3) / 1e9
     tops = ops / (mf_ms * 1e-3) / 1e12
     out = {"hbm_read_GBs": rd, "hbm_read_frac": rd / HBM_PEAK_GBS,
+           "hbm_read_56MiB_launch_GBs": rd7, "hbm_read_56MiB_launch_frac": rd7 / HBM_PEAK_GBS,
            "mfma_i8_TOPS": tops, "mfma_i8_frac": tops / INT8_PEAK_TOPS,
-           "how": "aql_measure_read over 512 MiB (2 buffers rotated); "
-                  "aql_measure_mfma_i8 (2048 waves x 16 x 20000 MFMAs)"}
+           "how": "aql_measure_read over 512 MiB (2 buffers rotated) and over 56 MiB "
+                  "(10 buffers rotated); aql_measure_mfma_i8 (2048 waves x 16 x 20000 MFMAs)"}
     say(out)
     return out
 

@@ -218,7 +218,7 @@ def test_w8a16_tiny():
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 15, 80), (1, 100, 960), (3, 33, 2560),
                                    (16, 64, 4112), (17, 50, 128), (33, 129, 256), (70, 40, 1024),
                                    (1, 9, 272), (1, 70, 16384), (1, 37, 16400), (1, 200, 20000),
-                                   (1, 4100, 48)])
+                                   (1, 4100, 48), (1, 70001, 32)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_shapes(M, N, K, with_bias):
     say("w8a16", M, N, K, with_bias)
@@ -351,7 +351,7 @@ def _dq8ca_case(x, w, wfmt, bias=None):
 
 @pytest.mark.parametrize("wfmt", [aql.AQL_W_Q8CSW, aql.AQL_W_Q4GSW])
 @pytest.mark.parametrize("M,N,K", [(1, 30, 64), (4, 100, 4096), (16, 17, 96), (17, 200, 256),
-                                   (128, 129, 512), (200, 64, 160)])
+                                   (128, 129, 512), (200, 64, 160), (40, 33, 32), (17, 1, 64)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
     say("dq8ca", wfmt, M, N, K, with_bias)
@@ -438,6 +438,15 @@ def test_w8a16_grouped_single_row_mixed_k():
     past the last channel."""
     g = workloads.gen(710)
     shapes = [(9, 4112), (2560, 960), (1, 16), (33, 2560), (100, 64), (70, 16384)]
+    _grouped_single_row(g, shapes)
+
+
+def test_w8a16_grouped_single_row_past_lds():
+    """As above with one K past the LDS budget for x: every wave then loads its x."""
+    _grouped_single_row(workloads.gen(711), [(9, 4112), (40, 16400), (2560, 960)])
+
+
+def _grouped_single_row(g, shapes):
     probs, refs = [], []
     for N, K in shapes:
         w = workloads.small_matrix(g, N, K, std=0.02)

@@ -37,16 +37,18 @@ __device__ __forceinline__ long unpack_q4x8(uint32_t w) {
 }
 
 // ------------------------------------------------------ streaming (M <= 16)
-// Bound by streaming the packed weights (and their group scales and sums) from
-// HBM. The access shape follows the weight-only GEMV: a wave instruction reads
-// 4 weight rows x 256 contiguous bytes, so each lane holds 16 bytes = one whole
-// 32-k group of one channel (lane % 4 = row, lane / 4 = group within the step),
-// plus that group's scale and sum (4 rows x 64 contiguous bytes each). The
-// group is multiplied where it lands with v_mfma_i32_4x4x4_i8: block b = lane / 4
-// takes k-slices of group b for 4 channels (B column j = lane % 4) against the
-// same k-slices of 4 rows of xq (A row i = lane % 4), so after 8 MFMAs lane
-// 4b + j holds, for each of its 4 rows, the exact int32 group sum of its own
-// channel: the zero point and the group scale are folded in right there.
+// Bound by streaming the packed weights and their group scales from HBM. The
+// access shape follows the weight-only GEMV: a wave instruction reads 4 weight
+// rows x 256 contiguous bytes, so each lane holds 16 bytes = one whole 32-k
+// group of one channel (lane % 4 = row, lane / 4 = group within the step),
+// plus that group's scale (4 rows x 64 contiguous bytes). The group is
+// multiplied where it lands with v_mfma_i32_4x4x4_i8: block b = lane / 4 takes
+// k-slices of group b for 4 channels (B column j = lane % 4) against the same
+// k-slices of 4 rows of xq (A row i = lane % 4), so after 8 MFMAs lane 4b + j
+// holds, for each of its 4 rows, the exact int32 group sum of its own channel.
+// The group's code sum comes from the unpacked bytes themselves (8 four-byte
+// dot products with ones, cheaper than streaming the stored sums), and the
+// zero point and the group scale are folded in right there.
 //
 // Tile: TG row groups of 4 channels, MB blocks of 4 rows of x, W waves splitting
 // K into 512-k steps (256 bytes of nibbles); batches of U steps ping-pong.
@@ -69,7 +71,6 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
   const int64_t mrows = p.M - m0 < 16 ? p.M - m0 : 16;
   const __amdgpu_buffer_rsrc_t rq = rsrc(p.q4 + n0 * KB, (uint32_t)(nrows * KB));
   const __amdgpu_buffer_rsrc_t rg = rsrc(p.gs + n0 * G, (uint32_t)(nrows * G * 4));
-  const __amdgpu_buffer_rsrc_t rm = rsrc(p.gsum + n0 * G, (uint32_t)(nrows * G * 4));
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq + m0 * K, (uint32_t)(mrows * K));
   const uint32_t qlane = (uint32_t)(j * KB + 16 * blk);
   const uint32_t glane = 4u * (uint32_t)(j * G + blk);
@@ -77,13 +78,13 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
   const int nst = (int)((KB + 255) >> 8);
   const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
 
-  int zp16[MB][4];
+  int zpn[MB][4];  // -zp per row (0 past M)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t mm = m0 + 4 * mb + v;
-      zp16[mb][v] = mm < p.M ? -16 * p.xz[mm] : 0;
+      zpn[mb][v] = mm < p.M ? -p.xz[mm] : 0;
     }
 
   f32x4 f[TG][MB];
@@ -95,7 +96,6 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
   struct Batch {
     i32x4 q[U][TG];
     float gs[U][TG];
-    int gm[U][TG];
     i32x4 x[U][MB][2];
   };
   auto fetch = [&](int i0, Batch &bt) {
@@ -115,7 +115,6 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
         bt.q[u][tg] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
         const int go = kin ? (int)(glane + 4u * (uint32_t)(4 * tg) * (uint32_t)G + gstep) : OOB;
         bt.gs[u][tg] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rg, go, 0, 2));
-        bt.gm[u][tg] = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, go, 0, 2);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
@@ -137,6 +136,14 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
           wq[2 * e] = (int)((w << 4) & 0xF0F0F0F0u);  // even k of the 8-k block, as 16 c
           wq[2 * e + 1] = (int)(w & 0xF0F0F0F0u);     // odd k
         }
+        // 16 x this lane's group sum of the codes, from the unpacked bytes: the
+        // same 8 MFMAs against an all-ones A operand (every row of the result
+        // holds the column sums); the matrix cores have room here, the vector
+        // ALU of these few waves does not
+        i32x4 ts = {0, 0, 0, 0};
+#pragma unroll
+        for (int d = 0; d < 8; ++d) ts = __builtin_amdgcn_mfma_i32_4x4x4i8(0x01010101, wq[d], ts, 0, 0, 0);
+        const int gm16 = ts[0];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           i32x4 t = {0, 0, 0, 0};
@@ -144,8 +151,8 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
           for (int d = 0; d < 8; ++d)
             t = __builtin_amdgcn_mfma_i32_4x4x4i8(bt.x[u][mb][d >> 2][d & 3], wq[d], t, 0, 0, 0);
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            f[tg][mb][v] += bt.gs[u][tg] * (float)(t[v] + __mul24(zp16[mb][v], bt.gm[u][tg]));
+          for (int v = 0; v < 4; ++v)  // |zp| <= 128, |gm16| <= 4096: 24-bit product
+            f[tg][mb][v] += bt.gs[u][tg] * (float)(t[v] + __mul24(zpn[mb][v], gm16));
         }
       }
   };
@@ -516,14 +523,15 @@ void launch_tiled(const Q4Args &a, hipStream_t st) {
 
 hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
   if (a.M <= kQ4StreamMaxM) {
-    // same launch-shape rule as the weight-only GEMV: 8-channel tiles for
-    // M <= 2, 16 otherwise; waves per workgroup until ~768 wave-tiles
+    // 8-channel tiles for M <= 2, 16 otherwise; waves per workgroup (splitting
+    // K) only while the wave-tiles are fewer than ~384: these waves are short
+    // and few, and a K split adds a cross-wave reduction to each
     const int MB = a.M <= 4 ? 1 : (a.M <= 8 ? 2 : 4);
     const int TG = a.M <= 2 ? 2 : 4;
     const int64_t nst = (a.K / 2 + 255) / 256;
     const int64_t tiles = (a.N + 4 * TG - 1) / (4 * TG);
     int W = 1;
-    while (W < 8 && tiles * W < 768 && W * 4 <= nst) W <<= 1;
+    while (W < 8 && tiles * W < 384 && W * 4 <= nst) W <<= 1;
     const dim3 grid((unsigned)tiles, 1);
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);

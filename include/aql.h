@@ -228,8 +228,9 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
  *   wq           device, int8 [N, K] (Q8CSW) or packed q4 [N, K/2] (Q4GSW)
  *   wscale       device, float32 [N] (Q8CSW) or [N, K/32] (Q4GSW)
  *   wsum         device, int32 [N] or [N, K/32]: sums of the codes (as written by
- *                the weight quantizer; the 4-bit kernel for M > 16 folds the zero
- *                point on the activation side and does not read them)
+ *                the weight quantizer). The Q4GSW kernels do not read them: they
+ *                form the group sums from the codes (M <= 16) or fold the zero
+ *                point on the activation side (M > 16)
  *   bias         device, [N] float32 (may be NULL)
  *   y            device, [M, N] float32 (output)
  *   x_scale_out  device, [M] float32 (optional output: the row scales)

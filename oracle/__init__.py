@@ -43,6 +43,8 @@ _SIGS = {
     "orc_linear_dq8ca": [_p, _i64, _i64, _int, _p, _p, _i64, _p, _i64, _p, _p, _p, _p, _p],
     "orc_linear_dq8ca_dequant_first": [_p, _p, _p, _i64, _i64, _int, _p, _p, _i64, _p,
                                        _i64, _p],
+    "orc_minmax_observe": [_p, _i64, _i64, _i64, _int, _f32, _i32, _p],
+    "orc_minmax_qparams": [_p, _p, _p],
 }
 
 
@@ -261,6 +263,58 @@ def linear_dq8ca_dequant_first(xq, xs, xz, wq, wscale, K, wfmt=W_Q8CSW, group=0,
                                                 _ptr(wq), _ptr(wscale), int(group), _ptr(b), N,
                                                 _ptr(y)), "linear_dq8ca_dequant_first")
     return y
+
+
+def minmax_empty():
+    """The running (min, max) of an observer that has seen nothing."""
+    return np.array([np.inf, -np.inf], np.float32)
+
+
+def minmax_observe(x, state, seq=0, residual=False, s1=0.0, z1=0):
+    """Fold x float32 [rows, cols] (or its two-pass residual against (s1, z1))
+    into the running (min, max) float32 [2]; returns the new state. seq > 0
+    skips the row at position 0 of every seq rows."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    st = np.array(state, np.float32).copy()
+    _check(lib().orc_minmax_observe(_ptr(x), rows, cols, seq, int(bool(residual)), s1, z1,
+                                    _ptr(st)), "minmax_observe")
+    return st
+
+
+def minmax_qparams(state):
+    """(scale, zero point) of a running (min, max) by the per-tensor affine rule."""
+    st = np.array(state, np.float32)
+    s = np.empty(1, np.float32)
+    z = np.empty(1, np.int32)
+    _check(lib().orc_minmax_qparams(_ptr(st), _ptr(s), _ptr(z)), "minmax_qparams")
+    return float(s[0]), int(z[0])
+
+
+def keep_outliers(amax, seam, nseams, factor):
+    """flashrt schemes, Fp8Static.decide with keep_outliers: the seams whose
+    largest point statistic exceeds factor times the median of all positive
+    statistics. amax: per point, NaN for a point without a statistic; seam:
+    the seam index of each point. Returns a list of nseams booleans. Written
+    with Python floats and statistics.median, as the page computes it."""
+    import math
+    import statistics
+    keep = [False] * nseams
+    if not factor:
+        return keep
+    values = [float(v) for v in amax if not math.isnan(v) and v > 0]
+    if not values:
+        return keep
+    median = statistics.median(values)
+    worst = [None] * nseams
+    for v, sidx in zip(amax, seam):
+        if math.isnan(v):
+            continue
+        if worst[sidx] is None or float(v) > worst[sidx]:
+            worst[sidx] = float(v)
+    for i in range(nseams):
+        keep[i] = worst[i] is not None and worst[i] > float(factor) * median
+    return keep
 
 
 def threads():

@@ -539,3 +539,65 @@ int orc_linear_dq8ca_dequant_first(const int8_t *xq, const float *xs,
     }
     return ORC_OK;
 }
+
+/* ---------------------------------------------------- static calibration */
+
+/*
+ * Running per-tensor (min, max) of a static activation observer,
+ * [SmolVLM q8 recipe] act_observer / Recorder / calibrate: state = {min, max},
+ * (+inf, -inf) before anything is observed, folded with every element fed.
+ * x is [rows, cols]; with seq > 0 the row at position 0 of every sequence of
+ * seq rows (r % seq == 0, the attention-sink position the Recorder drops) is
+ * skipped. residual != 0 observes the two-pass recipe's second run instead:
+ * r = x - fake_quant(x, s1, z1), fake_quant = (clamp(round(x * (1/s1)) + z1,
+ * -128, 127) - z1) * s1, each binary32 operation rounded on its own (the same
+ * residual the per-tensor activation quantizer above forms).
+ */
+int orc_minmax_observe(const float *x, int64_t rows, int64_t cols, int64_t seq,
+                       int residual, float s1, int32_t z1, float *state)
+{
+    if (rows < 0 || cols < 0 || seq < 0 || (residual && !(s1 > 0.0f))) return ORC_BAD;
+    const float inv1 = residual ? 1.0f / s1 : 0.0f;
+    const float fz1 = (float)z1;
+    float mn = state[0], mx = state[1];
+    for (int64_t r = 0; r < rows; ++r) {
+        if (seq > 0 && r % seq == 0) continue;
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = x[r * cols + c];
+            if (residual) {
+                float q = clampf_(rintf(v * inv1) + fz1, -128.0f, 127.0f);
+                float t = (q - fz1) * s1;
+                v = v - t;
+            }
+            if (v < mn) mn = v;
+            if (v > mx) mx = v;
+        }
+    }
+    state[0] = mn;
+    state[1] = mx;
+    return ORC_OK;
+}
+
+/*
+ * Per-tensor affine int8 qparams of an observer's (min, max),
+ * [SmolVLM q8 recipe] qparams (MinMaxObserver.calculate_qparams):
+ * mn = min(min, 0), mx = max(max, 0), s = max((mx - mn) / 255, FLT_EPSILON),
+ * z = clamp(-128 - round(mn / s), -128, 127), in binary32. An observer that
+ * saw nothing (min > max) gives the observer's defaults s = 1, z = 0.
+ */
+int orc_minmax_qparams(const float *state, float *scale, int32_t *zp)
+{
+    if (!(state[0] <= state[1])) {
+        *scale = 1.0f;
+        *zp = 0;
+        return ORC_OK;
+    }
+    float mn = state[0] < 0.0f ? state[0] : 0.0f;
+    float mx = state[1] > 0.0f ? state[1] : 0.0f;
+    float s = (mx - mn) / 255.0f;
+    if (s < FLT_EPSILON) s = FLT_EPSILON;
+    float zf = clampf_(-128.0f - rintf(mn / s), -128.0f, 127.0f);
+    *scale = s;
+    *zp = (int32_t)zf;
+    return ORC_OK;
+}

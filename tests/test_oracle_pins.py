@@ -463,3 +463,85 @@ def test_dq8ca_q4_exact_rational_brute_force():
                 for k in range(64))
             assert abs(Fraction(o["y"][m, n]) - exact) <= Fraction(1, 10**12) * Fraction(o["tol"][m, n])
     assert np.array_equal(gsum, codes.reshape(3, 2, 32).astype(np.int64).sum(axis=2))
+
+
+# ---------------------------------------------------------- static calibration
+
+
+def test_minmax_observe_matches_numpy_and_folds():
+    g = workloads.gen(30)
+    x = workloads.small_matrix(g, 37, 96, std=2.0).numpy()
+    x[0, 5] = 500.0    # rows 0, 12, 24, 36 start a 12-row sequence:
+    x[12, 3] = -400.0  # with seq = 12 they are not observed
+    st = oracle.minmax_observe(x, oracle.minmax_empty())
+    assert st[0] == x.min() and st[1] == x.max()
+    kept = np.array([r % 12 != 0 for r in range(x.shape[0])])
+    st = oracle.minmax_observe(x, oracle.minmax_empty(), seq=12)
+    assert st[0] == x[kept].min() and st[1] == x[kept].max()
+    assert st[1] < 500.0 and st[0] > -400.0
+    # observing in two calls is observing once
+    a = oracle.minmax_observe(x[:20], oracle.minmax_empty())
+    assert np.array_equal(oracle.minmax_observe(x[20:], a),
+                          oracle.minmax_observe(x, oracle.minmax_empty()))
+    # nothing observed: the state stays empty
+    st = oracle.minmax_observe(x[:1], oracle.minmax_empty(), seq=5)
+    assert st[0] == np.inf and st[1] == -np.inf
+
+
+def test_minmax_observe_residual_matches_torch_fake_quant():
+    """The second calibration run observes x - fake_quant(x, s1, z1); torch's
+    fake_quantize_per_tensor_affine is an independent implementation of that
+    fake quantizer (reciprocal scale, round half to even, clamp)."""
+    g = workloads.gen(31)
+    x = workloads.small_matrix(g, 50, 64, std=4.0).numpy()
+    x[3, :8] = 3000.0  # clipped by the first pass: a large residual
+    s1, z1 = oracle.minmax_qparams(oracle.minmax_observe(x[4:], oracle.minmax_empty()))
+    st = oracle.minmax_observe(x, oracle.minmax_empty(), residual=True, s1=s1, z1=z1)
+    xt = torch.from_numpy(x)
+    r = (xt - torch.fake_quantize_per_tensor_affine(xt, s1, z1, -128, 127)).numpy()
+    assert st[0] == r.min() and st[1] == r.max()
+    # rows the first pass does not clip leave residuals within half a step
+    st4 = oracle.minmax_observe(x[4:], oracle.minmax_empty(), residual=True, s1=s1, z1=z1)
+    assert max(-st4[0], st4[1]) <= 0.5 * s1 * (1 + 1e-5)
+
+
+def test_minmax_qparams_matches_observer():
+    g = workloads.gen(32)
+    base = workloads.small_matrix(g, 24, 40, std=3.0).numpy()
+    cases = [base, np.abs(base), -np.abs(base), np.zeros_like(base), base * 1e-30]
+    for x in cases:
+        ob = MinMaxObserver(dtype=torch.qint8, quant_min=-128, quant_max=127,
+                            qscheme=torch.per_tensor_affine)
+        st = oracle.minmax_empty()
+        for chunk in np.array_split(x, 3):  # several calibration batches
+            ob(torch.from_numpy(np.ascontiguousarray(chunk)))
+            st = oracle.minmax_observe(chunk, st)
+        ss, zz = ob.calculate_qparams()
+        assert oracle.minmax_qparams(st) == (ss.item(), zz.item())
+    # an observer that saw nothing returns its defaults
+    ob = MinMaxObserver(dtype=torch.qint8, quant_min=-128, quant_max=127,
+                        qscheme=torch.per_tensor_affine)
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        ss, zz = ob.calculate_qparams()
+    assert oracle.minmax_qparams(oracle.minmax_empty()) == (ss.item(), zz.item()) == (1.0, 0)
+
+
+def test_keep_outliers_worked_example():
+    """Worked by hand from the keep-outliers rule: the positive statistics of
+    all points are 1, 2, 3, 100, whose median is (2 + 3) / 2 = 2.5; at factor
+    20 the bar is 50, so only seam 2 (worst point 100) stays at host
+    precision; at factor 40 the bar is 100 and the comparison is strict."""
+    nan = float("nan")
+    amax = [1.0, 2.0, 3.0, nan, 100.0, 0.0, -1.0]
+    seam = [0, 0, 1, 1, 2, 3, 3]
+    assert oracle.keep_outliers(amax, seam, 5, 20.0) == [False, False, True, False, False]
+    assert oracle.keep_outliers(amax, seam, 5, 40.0) == [False] * 5
+    assert oracle.keep_outliers(amax, seam, 5, 0.0) == [False] * 5
+    # odd count: 1, 2, 3, 50, 100 -> median 3, bar 60: seam 2 kept, seam 1 (50) not
+    amax2 = amax + [50.0]
+    seam2 = seam + [1]
+    assert oracle.keep_outliers(amax2, seam2, 5, 20.0) == [False, False, True, False, False]
+    # no positive statistic: nothing to compare against
+    assert oracle.keep_outliers([nan, 0.0], [0, 1], 2, 20.0) == [False, False]

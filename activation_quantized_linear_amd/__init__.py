@@ -68,6 +68,10 @@ _SIGS = {
     "aql_gemm_i8_i32": ([_p, _p, _p, _i64, _i64, _i64, _p], _int),
     "aql_measure_read": ([_p, _i64, _p, _p], _int),
     "aql_measure_mfma_i8": ([_i64, _p, _p], _int),
+    "aql_minmax_reset": ([_p, _p], _int),
+    "aql_minmax_observe": ([_p, _i64, _i64, _i64, _int, _f32, _i32, _p, _p], _int),
+    "aql_minmax_qparams": ([_p, _p, _p, _p], _int),
+    "aql_keep_outliers": ([_p, _p, _i64, _i32, C.c_double, _p], _int),
     "aql_w8a16_group_table_bytes": ([_int], _sz),
     "aql_w8a16_group_plan": ([_p, _int, _p, _sz], _int),
     "aql_linear_w8a16_grouped": ([_p, _p, _p], _int),
@@ -305,6 +309,65 @@ def aql_linear_dq8ca(x, wq, wscale, wsum, wfmt=AQL_W_Q8CSW, group=0, bias=None, 
                                  int(group), _ptr(bias), N, _ptr(y), _ptr(x_scale_out),
                                  _ptr(x_zp_out), _ptr(ws), ws.numel(), _stream(dev)))
     return y
+
+
+# ------------------------------------------------------- static calibration
+
+
+def aql_minmax_state(device="cuda"):
+    """A new, empty running (min, max): device float32 [2] = (+inf, -inf)."""
+    st = torch.empty(2, dtype=torch.float32, device=device)
+    aql_minmax_reset(st)
+    return st
+
+
+def aql_minmax_reset(state):
+    _need(state, "state", torch.float32, 1)
+    _shape(state, "state", (2,))
+    _check("aql_minmax_reset", _lib.aql_minmax_reset(_ptr(state), _stream(state.device)))
+    return state
+
+
+def aql_minmax_observe(x, state, seq=0, residual=None):
+    """Fold x float32 [rows, cols] into the running (min, max) `state`. seq > 0
+    leaves out the row at position 0 of every seq rows; residual=(s1, z1)
+    observes x - fake_quant(x, s1, z1) instead (the two-pass recipe's second
+    calibration run)."""
+    _need(x, "x", torch.float32, 2)
+    _need(state, "state", torch.float32, 1, x.device)
+    _shape(state, "state", (2,))
+    rows, cols = x.shape
+    s1, z1 = residual if residual is not None else (0.0, 0)
+    _check("aql_minmax_observe",
+           _lib.aql_minmax_observe(_ptr(x), rows, cols, seq, int(residual is not None), s1, z1,
+                                   _ptr(state), _stream(x.device)))
+    return state
+
+
+def aql_minmax_qparams(state, scale=None, zp=None):
+    """-> (scale float32 [1], zp int32 [1]) device tensors by the per-tensor
+    affine observer rule."""
+    _need(state, "state", torch.float32, 1)
+    dev = state.device
+    scale = _out(scale, "scale", (1,), torch.float32, dev)
+    zp = _out(zp, "zp", (1,), torch.int32, dev)
+    _check("aql_minmax_qparams",
+           _lib.aql_minmax_qparams(_ptr(state), _ptr(scale), _ptr(zp), _stream(dev)))
+    return scale, zp
+
+
+def aql_keep_outliers(amax, seam, nseams, factor):
+    """Host decision, no GPU: list of nseams booleans (see aql.h)."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(amax, dtype=np.float32))
+    sidx = np.ascontiguousarray(np.asarray(seam, dtype=np.int32))
+    if a.shape != sidx.shape or a.ndim != 1:
+        raise ValueError("amax and seam must be 1-D of the same length")
+    keep = np.zeros(max(nseams, 0), np.int32)
+    _check("aql_keep_outliers",
+           _lib.aql_keep_outliers(a.ctypes.data_as(_p), sidx.ctypes.data_as(_p), a.size, nseams,
+                                  float(factor), keep.ctypes.data_as(_p)))
+    return [bool(v) for v in keep]
 
 
 def aql_measure_read(buf, sink):

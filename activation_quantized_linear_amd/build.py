@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaql.so")
 
-SOURCES = ["abi.cpp", "quant.hip", "w8a16.hip", "gemm_i8.hip", "dq8ca_q4.hip", "probe.hip", "w8a16_gemm.hip"]
+SOURCES = ["abi.cpp", "quant.hip", "w8a16.hip", "gemm_i8.hip", "dq8ca_q4.hip", "probe.hip",
+           "w8a16_gemm.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

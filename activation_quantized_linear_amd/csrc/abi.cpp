@@ -4,13 +4,16 @@
 // returns AQL_OK without a HIP call, and its (zero-element) buffers may be NULL.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "aql.h"
+#include "calib.h"
 #include "dq8ca_q4.h"
 #include "gemm_i8.h"
 #include "quant.h"
@@ -470,6 +473,72 @@ int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int
   g.N = N;
   g.K = K;
   return launched(aql::launch_gemm_i8(g, aql::EPI_RAW, false, (hipStream_t)stream), fn);
+}
+
+int aql_minmax_reset(float *state, void *stream) {
+  const char *fn = "aql_minmax_reset";
+  REQUIRE(state, AQL_ERR_NULL, "%s: state must not be NULL", fn);
+  REQUIRE(aligned16(state), AQL_ERR_ALIGN, "%s: state must be 16-byte aligned", fn);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_minmax_reset(state, (hipStream_t)stream), fn);
+}
+
+int aql_minmax_observe(const float *x, int64_t rows, int64_t cols, int64_t seq, int residual,
+                       float s1, int32_t z1, float *state, void *stream) {
+  const char *fn = "aql_minmax_observe";
+  REQUIRE(rows >= 0 && cols >= 0 && cols % 4 == 0 && seq >= 0, AQL_ERR_SHAPE,
+          "%s: need rows, seq >= 0 and cols >= 0 a multiple of 4 (rows=%lld cols=%lld seq=%lld)",
+          fn, (long long)rows, (long long)cols, (long long)seq);
+  REQUIRE(!residual || (finite_pos(s1) && z_ok(z1)), AQL_ERR_PARAM,
+          "%s: the residual needs s1 finite > 0 and z1 in [-128, 127]", fn);
+  REQUIRE(state, AQL_ERR_NULL, "%s: state must not be NULL", fn);
+  REQUIRE(aligned16(state) && aligned16(x), AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned",
+          fn);
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE(x, AQL_ERR_NULL, "%s: x must not be NULL", fn);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_minmax_observe(x, rows, cols, seq, residual != 0, s1, z1, state,
+                                             (hipStream_t)stream),
+                  fn);
+}
+
+int aql_minmax_qparams(const float *state, float *scale, int32_t *zp, void *stream) {
+  const char *fn = "aql_minmax_qparams";
+  REQUIRE(state && scale && zp, AQL_ERR_NULL, "%s: state, scale and zp must not be NULL", fn);
+  REQUIRE(aligned16(state) && aligned16(scale) && aligned16(zp), AQL_ERR_ALIGN,
+          "%s: pointers must be 16-byte aligned", fn);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_minmax_qparams(state, scale, zp, (hipStream_t)stream), fn);
+}
+
+int aql_keep_outliers(const float *amax, const int32_t *seam, int64_t npoints, int32_t nseams,
+                      double factor, int32_t *keep) {
+  const char *fn = "aql_keep_outliers";
+  REQUIRE(npoints >= 0 && nseams >= 0, AQL_ERR_SHAPE, "%s: counts must be >= 0", fn);
+  REQUIRE((npoints == 0 || (amax && seam)) && (nseams == 0 || keep), AQL_ERR_NULL,
+          "%s: arrays must not be NULL", fn);
+  for (int64_t p = 0; p < npoints; ++p)
+    REQUIRE(seam[p] >= 0 && seam[p] < nseams, AQL_ERR_PARAM,
+            "%s: point %lld names seam %d of %d", fn, (long long)p, (int)seam[p], (int)nseams);
+  for (int32_t i = 0; i < nseams; ++i) keep[i] = 0;
+  if (factor == 0.0) return ok();
+  std::vector<double> vals;
+  for (int64_t p = 0; p < npoints; ++p)
+    if (!std::isnan(amax[p]) && amax[p] > 0.0f) vals.push_back((double)amax[p]);
+  if (vals.empty()) return ok();
+  std::sort(vals.begin(), vals.end());
+  const size_t n = vals.size();
+  const double median = n % 2 ? vals[n / 2] : (vals[n / 2 - 1] + vals[n / 2]) / 2.0;
+  std::vector<double> worst((size_t)nseams, -INFINITY);
+  std::vector<char> seen((size_t)nseams, 0);
+  for (int64_t p = 0; p < npoints; ++p) {
+    if (std::isnan(amax[p])) continue;
+    const double v = (double)amax[p];
+    if (!seen[seam[p]] || v > worst[seam[p]]) worst[seam[p]] = v;
+    seen[seam[p]] = 1;
+  }
+  for (int32_t i = 0; i < nseams; ++i) keep[i] = seen[i] && worst[i] > factor * median;
+  return ok();
 }
 
 int aql_measure_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {

@@ -65,7 +65,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline")
     ap.add_argument("--only", default=None,
-                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant|copy)")
+                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant|calib|copy)")
     ap.add_argument("--no-settle", action="store_true",
                     help="profile helper: skip the settle phase (counter runs serialize every "
                          "dispatch, so settling there only costs time)")
@@ -352,6 +352,29 @@ def sec_quant(torch, aql, workloads, dev):
     return [row]
 
 
+def sec_calib(torch, aql, workloads, dev):
+    """Static calibration: one observer call over a batch of 4096 rows of the
+    W8A8 workload's width, plain and residual (the two-pass second run)."""
+    rows, cols = 4096, 4096
+    ncopy = copies_for(4 * rows * cols)
+    g = workloads.gen(77)
+    xs = [workloads.small_matrix(g, rows, cols, std=4.0).to(dev) for _ in range(ncopy)]
+    st = aql.aql_minmax_state(dev)
+    out = []
+    for residual in (None, (0.05, 3)):
+        fn = lambda i: aql.aql_minmax_observe(xs[i], st, residual=residual)
+        for i in range(ncopy):
+            fn(i)
+        med, _ = event_time_ms(torch, fn, 40, ncopy)
+        nb = 4 * rows * cols
+        row = {"workload": f"calibration observe{' residual' if residual else ''} fp32 "
+                           f"{rows}x{cols}", "us": med * 1e3, "GB/s": nb / (med * 1e-3) / 1e9,
+               "frac_hbm": nb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        say(row)
+        out.append(row)
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline
 
 
@@ -474,7 +497,7 @@ def main():
     secondary = []
     if args.only is not None and args.only != "sweep":
         fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant,
-              "copy": sec_copy}[args.only]
+              "calib": sec_calib, "copy": sec_copy}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
         return
     calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
@@ -484,7 +507,7 @@ def main():
     del calls
     torch.cuda.empty_cache()
     if args.only is None and not args.no_secondary:
-        for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant):
+        for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant, sec_calib):
             secondary += fn(torch, aql, workloads, dev)
             torch.cuda.empty_cache()
 

@@ -303,6 +303,56 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
 int aql_gemm_i8_i32(const int8_t *a, const int8_t *b, int32_t *c, int64_t M, int64_t N,
                     int64_t K, void *stream);
 
+/* ------------------------------------------------------ static calibration */
+
+/*
+ * Static per-tensor activation qparams, calibrated on the device
+ * ([SmolVLM q8 recipe] act_observer, Recorder, calibrate, qparams): one
+ * running (min, max) per observed activation, folded over any number of
+ * calibration batches, then turned into the per-tensor affine int8 (s, z)
+ * that aql_linear_q8ta_q8csw takes. A two-pass linear's second pair
+ * (s2, z2) comes from a second observer fed with each input's first-pass
+ * rounding error.
+ *
+ * state: device float32[2] = {min, max}; (+inf, -inf) is the empty observer.
+ * All calls are ordered on `stream` and allocate nothing.
+ *
+ * aql_minmax_reset: state = (+inf, -inf).
+ *
+ * aql_minmax_observe: state = (min(state.min, min x), max(state.max, max x))
+ * over x [rows, cols] float32, row-major. With seq > 0, row r is at position
+ * r % seq of its sequence and the rows at position 0 are not observed (the
+ * recipe's Recorder drops the attention-sink position). With residual != 0
+ * each element is replaced by x - (clamp(round(x * (1/s1)) + z1, -128, 127)
+ * - z1) * s1, the rounding error of the first pass formed exactly as
+ * aql_quantize_act_per_tensor forms it. NaN elements are ignored.
+ * Errors: rows < 0, seq < 0, cols < 0 or cols % 4 != 0; residual with s1 not
+ * finite and positive or z1 outside [-128, 127]; NULL or misaligned x
+ * (rows, cols > 0) / state.
+ *
+ * aql_minmax_qparams: scale[0], zp[0] from state by MinMaxObserver's
+ * per-tensor affine rule: mn = min(min, 0), mx = max(max, 0),
+ * s = max((mx - mn) / 255, FLT_EPSILON), z = clamp(-128 - round(mn / s),
+ * -128, 127); an observer that saw nothing gives (1, 0). Device outputs.
+ * Errors: NULL or misaligned pointers.
+ *
+ * aql_keep_outliers (host, no GPU): the keep-at-host-precision decision of
+ * [flashrt schemes] Fp8Static.keep_outliers. amax[p] is the statistic of
+ * point p (NaN: the point has none), seam[p] in [0, nseams) the seam that owns
+ * it. With m the median of all positive statistics (the mean of the two
+ * middle ones for an even count), keep[s] = 1 when the largest statistic of
+ * seam s exceeds factor * m; factor 0, or no positive statistic, keeps
+ * nothing. Arithmetic in double, as the page's Python floats.
+ * Errors: npoints or nseams < 0; NULL arrays for non-zero counts; a seam
+ * index out of range.
+ */
+int aql_minmax_reset(float *state, void *stream);
+int aql_minmax_observe(const float *x, int64_t rows, int64_t cols, int64_t seq, int residual,
+                       float s1, int32_t z1, float *state, void *stream);
+int aql_minmax_qparams(const float *state, float *scale, int32_t *zp, void *stream);
+int aql_keep_outliers(const float *amax, const int32_t *seam, int64_t npoints, int32_t nseams,
+                      double factor, int32_t *keep);
+
 /* ---------------------------------------------------- measurement helpers */
 
 /*

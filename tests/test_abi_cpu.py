@@ -162,6 +162,56 @@ def test_measure_helpers_validation():
     assert m(4, MIS, None) == aql.AQL_ERR_ALIGN
 
 
+def test_calibration_validation():
+    o = L.aql_minmax_observe
+    st = C.c_void_p(0x40000)
+    assert o(A, 4, 6, 0, 0, 0.0, 0, st, None) == aql.AQL_ERR_SHAPE      # cols % 4
+    assert o(A, -1, 8, 0, 0, 0.0, 0, st, None) == aql.AQL_ERR_SHAPE
+    assert o(A, 4, 8, -2, 0, 0.0, 0, st, None) == aql.AQL_ERR_SHAPE
+    assert o(A, 4, 8, 0, 1, 0.0, 0, st, None) == aql.AQL_ERR_PARAM      # residual needs s1 > 0
+    assert o(A, 4, 8, 0, 1, 0.5, 128, st, None) == aql.AQL_ERR_PARAM
+    assert o(A, 4, 8, 0, 1, float("inf"), 0, st, None) == aql.AQL_ERR_PARAM
+    assert o(A, 4, 8, 0, 0, 0.0, 0, NUL, None) == aql.AQL_ERR_NULL
+    assert o(NUL, 4, 8, 0, 0, 0.0, 0, st, None) == aql.AQL_ERR_NULL
+    assert o(MIS, 4, 8, 0, 0, 0.0, 0, st, None) == aql.AQL_ERR_ALIGN
+    assert o(NUL, 0, 8, 0, 0, 0.0, 0, st, None) == aql.AQL_OK            # empty: no-op
+    assert L.aql_minmax_reset(NUL, None) == aql.AQL_ERR_NULL
+    assert L.aql_minmax_reset(MIS, None) == aql.AQL_ERR_ALIGN
+    assert L.aql_minmax_qparams(st, NUL, Y, None) == aql.AQL_ERR_NULL
+    assert L.aql_minmax_qparams(st, A, MIS, None) == aql.AQL_ERR_ALIGN
+    k = L.aql_keep_outliers
+    keep = (C.c_int32 * 2)()
+    amax = (C.c_float * 2)(1.0, 2.0)
+    seam = (C.c_int32 * 2)(0, 2)
+    assert k(amax, seam, 2, 2, 20.0, keep) == aql.AQL_ERR_PARAM           # seam 2 of 2
+    assert k(amax, seam, -1, 2, 20.0, keep) == aql.AQL_ERR_SHAPE
+    assert k(NUL, seam, 2, 2, 20.0, keep) == aql.AQL_ERR_NULL
+    assert k(NUL, NUL, 0, 0, 20.0, NUL) == aql.AQL_OK
+
+
+def test_keep_outliers_matches_oracle():
+    """The host decision against the oracle's, on random statistics with
+    missing points, non-positive values, ties and both count parities."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        npts = int(rng.integers(0, 30))
+        nseams = int(rng.integers(1, 8))
+        amax = rng.lognormal(0.0, 2.0, npts).astype(np.float32)
+        amax[rng.random(npts) < 0.1] = np.nan
+        amax[rng.random(npts) < 0.1] = 0.0
+        amax[rng.random(npts) < 0.05] = -1.0
+        if npts > 3 and trial % 7 == 0:
+            amax[1] = amax[0]  # a tie
+        seam = rng.integers(0, nseams, npts).astype(np.int32)
+        factor = float(rng.choice([0.0, 1.0, 5.0, 20.0]))
+        got = aql.aql_keep_outliers(amax, seam, nseams, factor)
+        want = oracle.keep_outliers([float(v) for v in amax], [int(v) for v in seam], nseams,
+                                    factor)
+        assert got == want, (trial, amax, seam, factor)
+
+
 def test_valid_call_without_gpu_reports_device():
     """On a host without a gfx950, a valid non-empty call fails with
     AQL_ERR_DEVICE before launching anything."""

@@ -488,3 +488,61 @@ def test_w8a16_grouped_smolvlm_sweep_in_graph():
         torch.cuda.synchronize()
         for p, (yref, tol) in zip(probs, expect):
             check_float(host(p[4].float()), yref, tol, BF16, f"graph replay {rep}")
+
+
+# ---------------------------------------------------------- static calibration
+
+
+def _observe_case(x, batches, seq=0, residual=None):
+    """Device observer over row batches of x vs the oracle's, bit for bit."""
+    st = aql.aql_minmax_state(DEV)
+    ost = oracle.minmax_empty()
+    for part in np.array_split(np.arange(x.shape[0]), batches):
+        xb = x[part[0]:part[-1] + 1] if len(part) else x[:0]
+        aql.aql_minmax_observe(dev(xb), st, seq=seq, residual=residual)
+        r = {} if residual is None else dict(residual=True, s1=residual[0], z1=residual[1])
+        ost = oracle.minmax_observe(xb.numpy(), ost, seq=seq, **r)
+    got = host(st)
+    assert np.array_equal(got, ost), (got, ost)
+    s, z = aql.aql_minmax_qparams(st)
+    assert (float(host(s)[0]), int(host(z)[0])) == oracle.minmax_qparams(ost)
+    return got
+
+
+@pytest.mark.parametrize("rows,cols,batches,seq", [(1, 4, 1, 0), (37, 96, 3, 12), (300, 1028, 5, 0),
+                                                   (64, 4096, 2, 16), (5, 8, 1, 5)])
+def test_minmax_observe(rows, cols, batches, seq):
+    say("minmax observe", rows, cols, batches, seq)
+    g = workloads.gen(900 + rows + cols)
+    x = workloads.small_matrix(g, rows, cols, std=3.0)
+    if rows > 13:
+        x[12, 1] = 1e4   # at position 0 of a 12-row sequence
+        x[13, 2] = -7e3
+    _observe_case(x, batches, seq)
+
+
+def test_minmax_empty_and_qparams_defaults():
+    st = aql.aql_minmax_state(DEV)
+    x = torch.zeros(0, 64, dtype=torch.float32, device=DEV)
+    aql.aql_minmax_observe(x, st)
+    # one row, at position 0 of its sequence: not observed
+    aql.aql_minmax_observe(torch.ones(1, 8, dtype=torch.float32, device=DEV), st, seq=5)
+    s, z = aql.aql_minmax_qparams(st)
+    assert float(host(s)[0]) == 1.0 and int(host(z)[0]) == 0
+    assert np.array_equal(host(st), oracle.minmax_empty())
+
+
+def test_two_pass_calibration_on_the_workload():
+    """The static two-pass calibration of the W8A8 workload: the first
+    observer (sink row left out) reproduces the workload's (s1, z1), the second
+    observes the first pass's rounding error; both bit for bit with the oracle."""
+    d = workloads.two_pass(seed=0)
+    x = d["x"]
+    M = x.shape[0]
+    st1 = _observe_case(x, 1, seq=M)  # one call: the workload is one 512-token sequence
+    s1, z1 = oracle.minmax_qparams(st1)
+    cs, cz, _ = oracle.choose_qparams_rows(x[1:].reshape(1, -1).numpy(), quantize=False)
+    assert (s1, z1) == (float(cs[0]), int(cz[0]))
+    st2 = _observe_case(x, 1, seq=M, residual=(s1, z1))
+    s2, _ = oracle.minmax_qparams(st2)
+    assert 0 < s2 < s1 / 100  # the residual spans about one first-pass step

@@ -44,6 +44,9 @@ _SIGS = {
     "orc_linear_dq8ca_dequant_first": [_p, _p, _p, _i64, _i64, _int, _p, _p, _i64, _p,
                                        _i64, _p],
     "orc_minmax_observe": [_p, _i64, _i64, _i64, _int, _f32, _i32, _p],
+    "orc_gptq_damp": [_p, _i64, C.c_double, _p, _p],
+    "orc_gptq_hinv": [_p, _i64, _p],
+    "orc_gptq_quantize": [_p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p, _p],
     "orc_minmax_qparams": [_p, _p, _p],
 }
 
@@ -315,6 +318,48 @@ def keep_outliers(amax, seam, nseams, factor):
     for i in range(nseams):
         keep[i] = worst[i] is not None and worst[i] > float(factor) * median
     return keep
+
+
+def gptq_damped(H, damp=0.01):
+    """(damped Hessian float64 [K, K], dead columns bool [K]) of gptq_int8."""
+    H = _c(H, np.float64)
+    K = H.shape[0]
+    Hd = np.empty_like(H)
+    dead = np.empty(K, np.uint8)
+    _check(lib().orc_gptq_damp(_ptr(H), K, damp, _ptr(Hd), _ptr(dead)), "gptq_damp")
+    return Hd, dead.astype(bool)
+
+
+def gptq_hinv(Hd):
+    """Upper factor hinv of Hd^-1 (hinv^T hinv = Hd^-1), float64 [K, K]."""
+    Hd = _c(Hd, np.float64)
+    K = Hd.shape[0]
+    hinv = np.empty_like(Hd)
+    _check(lib().orc_gptq_hinv(_ptr(Hd), K, _ptr(hinv)), "gptq_hinv")
+    return hinv
+
+
+def gptq_int8(w, H, damp=0.01, block=128, rows=None, hinv=None):
+    """GPTQ int8 codes: w float32 [N, K], H float64 [K, K] -> (q int8, scale
+    float32 [N], wsum int32). rows: compute only these rows (q, wsum then hold
+    them in that order; scale stays [N]). hinv: reuse a factor from gptq_hinv
+    of the same damped Hessian."""
+    w = _c(w, np.float32)
+    N, K = w.shape
+    _, scale, _ = quantize_weight_int8(w, WQ_SYM127_5)
+    Hd, dead = gptq_damped(H, damp)
+    if hinv is None:
+        hinv = gptq_hinv(Hd)
+    hinv = _c(hinv, np.float64)
+    dead8 = dead.astype(np.uint8)
+    rl = None if rows is None else np.ascontiguousarray(np.asarray(rows, np.int64))
+    R = N if rl is None else rl.size
+    q = np.empty((R, K), np.int8)
+    wsum = np.empty(R, np.int32)
+    _check(lib().orc_gptq_quantize(_ptr(w), N, K, _ptr(dead8), _ptr(hinv), _ptr(scale), block,
+                                   _ptr(rl), 0 if rl is None else rl.size, _ptr(q), _ptr(wsum)),
+           "gptq_quantize")
+    return q, scale, wsum
 
 
 def threads():

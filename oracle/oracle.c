@@ -601,3 +601,160 @@ int orc_minmax_qparams(const float *state, float *scale, int32_t *zp)
     *zp = (int32_t)zf;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------- GPTQ */
+
+/*
+ * GPTQ for the int8 weight grid, [SmolVLM q8 recipe] gptq_int8 (Frantar et al.),
+ * in binary64 throughout. The page leaves the order of its library reductions
+ * (Cholesky, the inverse, the block product, the diagonal mean) to LAPACK/BLAS;
+ * the reading here fixes each to a plain ascending sum that starts at 0 and is
+ * subtracted (or used) once complete, with every multiply and add rounded on
+ * its own:
+ *
+ *   chol(A) = L lower, column by column: L[j][j] = sqrt(A[j][j] - sum_{k<j}
+ *     L[j][k]^2), L[i][j] = (A[i][j] - sum_{k<j} L[i][k] L[j][k]) / L[j][j];
+ *   X = L^-1 row by row: X[j][j] = 1 / L[j][j], X[i][j] = -(sum_{k=j}^{i-1}
+ *     L[i][k] X[k][j]) / L[i][i];
+ *   A^-1 = X^T X: (A^-1)[i][j] = sum_{k>=max(i,j)} X[k][i] X[k][j];
+ *   hinv = chol(H^-1)^T (upper, hinv^T hinv = H^-1).
+ *
+ * Matrices are row-major double; L, X, A^-1 are K x K. Returns ORC_BAD if a
+ * pivot is not positive (H not positive definite after damping).
+ */
+static int chol_lower_(const double *A, int64_t K, double *L)
+{
+    for (int64_t i = 0; i < K * K; ++i) L[i] = 0.0;
+    for (int64_t j = 0; j < K; ++j) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < j; ++k) acc = acc + L[j * K + k] * L[j * K + k];
+        const double d = A[j * K + j] - acc;
+        if (!(d > 0.0)) return ORC_BAD;
+        const double ljj = sqrt(d);
+        L[j * K + j] = ljj;
+#pragma omp parallel for schedule(static)
+        for (int64_t i = j + 1; i < K; ++i) {
+            double a = 0.0;
+            for (int64_t k = 0; k < j; ++k) a = a + L[i * K + k] * L[j * K + k];
+            L[i * K + j] = (A[i * K + j] - a) / ljj;
+        }
+    }
+    return ORC_OK;
+}
+
+/* hinv (upper, row-major) of the damped Hessian Hd: chol(chol_inverse(chol(Hd)))^T. */
+int orc_gptq_hinv(const double *Hd, int64_t K, double *hinv)
+{
+    if (K <= 0) return ORC_BAD;
+    double *L = malloc(sizeof(double) * K * K);
+    double *X = malloc(sizeof(double) * K * K);
+    double *Ai = malloc(sizeof(double) * K * K);
+    int rc = ORC_BAD;
+    if (!L || !X || !Ai) goto out;
+    if (chol_lower_(Hd, K, L) != ORC_OK) goto out;
+    for (int64_t i = 0; i < K * K; ++i) X[i] = 0.0;
+    for (int64_t i = 0; i < K; ++i) {
+        X[i * K + i] = 1.0 / L[i * K + i];
+#pragma omp parallel for schedule(static)
+        for (int64_t j = 0; j < i; ++j) {
+            double a = 0.0;
+            for (int64_t k = j; k < i; ++k) a = a + L[i * K + k] * X[k * K + j];
+            X[i * K + j] = -a / L[i * K + i];
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < K; ++j) {
+            const int64_t k0 = i > j ? i : j;
+            double a = 0.0;
+            for (int64_t k = k0; k < K; ++k) a = a + X[k * K + i] * X[k * K + j];
+            Ai[i * K + j] = a;
+        }
+    if (chol_lower_(Ai, K, L) != ORC_OK) goto out;
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t j = 0; j < K; ++j) hinv[i * K + j] = L[j * K + i];
+    rc = ORC_OK;
+out:
+    free(L);
+    free(X);
+    free(Ai);
+    return rc;
+}
+
+/*
+ * The damped Hessian of gptq_int8: dead = (H[d][d] == 0) gets H[d][d] = 1 and
+ * its weight column zeroed (done by the caller), then damp * mean(diag H) is
+ * added to the diagonal, the mean an ascending sum divided by K.
+ */
+int orc_gptq_damp(const double *H, int64_t K, double damp, double *Hd, uint8_t *dead)
+{
+    if (K <= 0) return ORC_BAD;
+    for (int64_t i = 0; i < K * K; ++i) Hd[i] = H[i];
+    for (int64_t k = 0; k < K; ++k) {
+        dead[k] = Hd[k * K + k] == 0.0;
+        if (dead[k]) Hd[k * K + k] = 1.0;
+    }
+    double sum = 0.0;
+    for (int64_t k = 0; k < K; ++k) sum = sum + Hd[k * K + k];
+    const double c = damp * (sum / (double)K);
+    for (int64_t k = 0; k < K; ++k) Hd[k * K + k] = Hd[k * K + k] + c;
+    return ORC_OK;
+}
+
+/*
+ * gptq_int8 proper, given hinv and the per-channel scales (the SYM127_5 weight
+ * quantizer's, amax / 127.5 in binary32, used as doubles). Columns in blocks of
+ * `block`; inside a block column i of row n: qc = clamp(round(w/s), -128, 127)
+ * (round half to even), e = (w - qc s) / hinv[i][i], then w[j] -= e hinv[i][j]
+ * for the block's columns j >= i; after the block, w[j] -= sum_t e_t hinv[t][j]
+ * for every later column j (the ascending dot product over the block's t,
+ * subtracted once). Rows are independent. wsum (may be NULL) = sum of codes.
+ * rows: a list of the rows to compute (NULL: all N, written at their index);
+ * with a list, row r of the output is row rows[r] of w.
+ */
+int orc_gptq_quantize(const float *w, int64_t N, int64_t K, const uint8_t *dead,
+                      const double *hinv, const float *scale, int64_t block,
+                      const int64_t *rows, int64_t nrows, int8_t *q, int32_t *wsum)
+{
+    if (N < 0 || K <= 0 || block <= 0) return ORC_BAD;
+    const int64_t R = rows ? nrows : N;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t n = rows ? rows[r] : r;
+        double *wr = malloc(sizeof(double) * K);
+        double *err = malloc(sizeof(double) * block);
+        if (!wr || !err) {
+            bad = 1;
+            free(wr);
+            free(err);
+            continue;
+        }
+        const double s = (double)scale[n];
+        for (int64_t k = 0; k < K; ++k) wr[k] = dead[k] ? 0.0 : (double)w[n * K + k];
+        int64_t total = 0;
+        for (int64_t i1 = 0; i1 < K; i1 += block) {
+            const int64_t i2 = i1 + block < K ? i1 + block : K;
+            for (int64_t i = i1; i < i2; ++i) {
+                const double col = wr[i];
+                double qc = nearbyint(col / s);
+                if (qc < -128.0) qc = -128.0;
+                if (qc > 127.0) qc = 127.0;
+                q[r * K + i] = (int8_t)(int)qc;
+                total += (int)qc;
+                const double e = (col - qc * s) / hinv[i * K + i];
+                for (int64_t j = i; j < i2; ++j) wr[j] = wr[j] - e * hinv[i * K + j];
+                err[i - i1] = e;
+            }
+            for (int64_t j = i2; j < K; ++j) {
+                double a = 0.0;
+                for (int64_t t = i1; t < i2; ++t) a = a + err[t - i1] * hinv[t * K + j];
+                wr[j] = wr[j] - a;
+            }
+        }
+        if (wsum) wsum[r] = (int32_t)total;
+        free(wr);
+        free(err);
+    }
+    return bad ? ORC_BAD : ORC_OK;
+}

@@ -545,3 +545,96 @@ def test_keep_outliers_worked_example():
     assert oracle.keep_outliers(amax2, seam2, 5, 20.0) == [False, False, True, False, False]
     # no positive statistic: nothing to compare against
     assert oracle.keep_outliers([nan, 0.0], [0, 1], 2, 20.0) == [False, False]
+
+
+# ------------------------------------------------------------------- GPTQ
+
+
+def _spd_hessian(g, K, rows, dead=()):
+    X = workloads.small_matrix(g, rows, K).double()
+    for d in dead:
+        X[:, d] = 0.0
+    return (X.T @ X).numpy()
+
+
+def test_gptq_hinv_is_the_upper_factor_of_the_inverse():
+    g = workloads.gen(40)
+    H = _spd_hessian(g, 48, 200)
+    Hd, dead = oracle.gptq_damped(H, 0.01)
+    assert not dead.any()
+    assert np.allclose(np.diag(Hd) - np.diag(H), 0.01 * np.mean(np.diag(H)), rtol=1e-12)
+    hinv = oracle.gptq_hinv(Hd)
+    assert np.array_equal(hinv, np.triu(hinv)) and np.all(np.diag(hinv) > 0)
+    ref = np.linalg.cholesky(np.linalg.inv(Hd)).T  # numpy's LAPACK, independent
+    assert np.allclose(hinv, ref, rtol=1e-9, atol=1e-12 * np.abs(ref).max())
+    assert np.allclose(hinv.T @ hinv @ Hd, np.eye(48), atol=1e-9)
+
+
+def test_gptq_identity_hessian_is_round_to_nearest():
+    """With H = I the factor is diagonal and no rounding error is passed on:
+    GPTQ is plain round-to-nearest of w / s in binary64."""
+    g = workloads.gen(41)
+    w = workloads.small_matrix(g, 30, 70, std=0.02).numpy()
+    q, s, wsum = oracle.gptq_int8(w, np.eye(70), block=16)
+    ref = np.clip(np.rint(w.astype(np.float64) / s[:, None].astype(np.float64)), -128, 127)
+    assert np.array_equal(q, ref.astype(np.int8))
+    assert np.array_equal(wsum, q.astype(np.int64).sum(1))
+    _, s_rtn, _ = oracle.quantize_weight_int8(w, oracle.WQ_SYM127_5)
+    assert np.array_equal(s, s_rtn)  # the scales are the SYM127_5 quantizer's
+
+
+def _gptq_unblocked_torch(w, H, damp=0.01):
+    """GPTQ without lazy blocks (every rounding error is pushed onto all later
+    columns at once), its factor from torch's own Cholesky and inverse: equal
+    to the blocked algorithm in exact arithmetic."""
+    _, s, _ = oracle.quantize_weight_int8(w, oracle.WQ_SYM127_5)
+    W = torch.from_numpy(w).double().clone()
+    Ht = torch.from_numpy(H).double().clone()
+    K = W.shape[1]
+    dead = torch.diag(Ht) == 0
+    Ht[dead, dead] = 1.0
+    W[:, dead] = 0.0
+    Ht += damp * torch.mean(torch.diag(Ht)) * torch.eye(K, dtype=torch.float64)
+    U = torch.linalg.cholesky(torch.linalg.inv(Ht)).T
+    sc = torch.from_numpy(s).double()
+    Q = torch.zeros_like(W)
+    for i in range(K):
+        Q[:, i] = torch.clamp(torch.round(W[:, i] / sc), -128, 127)
+        e = (W[:, i] - Q[:, i] * sc) / U[i, i]
+        W[:, i:] -= e[:, None] * U[i, i:][None, :]
+    return Q.numpy().astype(np.int8)
+
+
+def test_gptq_matches_unblocked_torch_reference():
+    g = workloads.gen(42)
+    K, N = 96, 40
+    H = _spd_hessian(g, K, 300, dead=(5, 77))
+    w = workloads.small_matrix(g, N, K, std=0.02).numpy()
+    q, _, _ = oracle.gptq_int8(w, H, block=32)
+    ref = _gptq_unblocked_torch(w, H)
+    diff = q.astype(np.int32) - ref.astype(np.int32)
+    # reduction orders differ (LAPACK vs plain sums, lazy vs eager updates):
+    # only near-ties may round the other way, by one code
+    assert np.abs(diff).max() <= 1 and (diff != 0).mean() < 0.002
+    assert np.all(q[:, [5, 77]] == 0)  # dead columns
+
+
+def test_gptq_lowers_the_hessian_weighted_error():
+    """What GPTQ is for: its codes reproduce X W^T better than round-to-nearest."""
+    g = workloads.gen(43)
+    K, N = 128, 64
+    Z = workloads.small_matrix(g, 400, K).double().numpy()
+    mix = workloads.small_matrix(g, K, K).double().numpy()
+    X = Z @ (np.eye(K) + 0.3 * mix)  # correlated input channels, as real activations are
+    X[:, :8] *= 6.0                  # and a few dominant ones
+    H = X.T @ X
+    w = workloads.small_matrix(g, N, K, std=0.02).numpy()
+    q, s, _ = oracle.gptq_int8(w, H, block=32)
+    qr, sr, _ = oracle.quantize_weight_int8(w, oracle.WQ_SYM127_5)
+    W = w.astype(np.float64)
+    e_gptq = np.linalg.norm(X @ (W - q * s[:, None].astype(np.float64)).T)
+    e_rtn = np.linalg.norm(X @ (W - qr * sr[:, None].astype(np.float64)).T)
+    assert e_gptq < 0.9 * e_rtn
+    # the block size changes only the rounding of the updates
+    q2, _, _ = oracle.gptq_int8(w, H, block=128)
+    assert (q2 != q).mean() < 0.002

@@ -36,6 +36,7 @@ AQL_W_Q8CSW = 0
 AQL_W_Q4GSW = 1
 AQL_OP_Q8TA_Q8CSW = 1
 AQL_OP_DQ8CA = 2
+AQL_OP_GPTQ_INT8 = 3
 AQL_MAX_K_INT8 = 65536
 
 if not os.path.exists(LIB_PATH):
@@ -72,6 +73,8 @@ _SIGS = {
     "aql_minmax_observe": ([_p, _i64, _i64, _i64, _int, _f32, _i32, _p, _p], _int),
     "aql_minmax_qparams": ([_p, _p, _p, _p], _int),
     "aql_keep_outliers": ([_p, _p, _i64, _i32, C.c_double, _p], _int),
+    "aql_gptq_int8": ([_p, _i64, _i64, _p, C.c_double, _i64, _p, _p, _p, _p, _p, _p, _sz, _p],
+                      _int),
     "aql_w8a16_group_table_bytes": ([_int], _sz),
     "aql_w8a16_group_plan": ([_p, _int, _p, _sz], _int),
     "aql_linear_w8a16_grouped": ([_p, _p, _p], _int),
@@ -368,6 +371,36 @@ def aql_keep_outliers(amax, seam, nseams, factor):
            _lib.aql_keep_outliers(a.ctypes.data_as(_p), sidx.ctypes.data_as(_p), a.size, nseams,
                                   float(factor), keep.ctypes.data_as(_p)))
     return [bool(v) for v in keep]
+
+
+# ---------------------------------------------------------------- GPTQ int8
+
+
+def aql_gptq_int8(w, H, damp=0.01, block=128, q=None, scale=None, wsum=None, hinv=False,
+                  info=None, workspace=None):
+    """GPTQ int8 codes on the device. w float32 [N, K], H float64 [K, K] ->
+    (q int8 [N, K], scale float32 [N], wsum int32 [N], hinv float64 [K, K] or
+    None, info int32 [1]). hinv=True also returns the upper factor of the
+    damped Hessian's inverse. info (device) is 0 on success, else the failed
+    pivot (see aql.h); it is not read back here, so the call stays
+    asynchronous."""
+    _need(w, "w", torch.float32, 2)
+    dev = w.device
+    N, K = w.shape
+    _need(H, "H", torch.float64, 2, dev)
+    _shape(H, "H", (K, K))
+    q = _out(q, "q", (N, K), torch.int8, dev)
+    scale = _out(scale, "scale", (N,), torch.float32, dev)
+    wsum = _out(wsum, "wsum", (N,), torch.int32, dev)
+    hv = torch.empty((K, K), dtype=torch.float64, device=dev) if hinv else None
+    info = _out(info, "info", (1,), torch.int32, dev)
+    nbytes = aql_workspace_bytes(AQL_OP_GPTQ_INT8, block, N, K)
+    ws = _workspace(workspace, nbytes, dev)
+    _check("aql_gptq_int8",
+           _lib.aql_gptq_int8(_ptr(w), N, K, _ptr(H), float(damp), int(block), _ptr(q),
+                              _ptr(scale), _ptr(wsum), _ptr(hv), _ptr(info), _ptr(ws),
+                              ws.numel(), _stream(dev)))
+    return q, scale, wsum, hv, info
 
 
 def aql_measure_read(buf, sink):

@@ -17,7 +17,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libaql.so")
 
 SOURCES = ["abi.cpp", "quant.hip", "w8a16.hip", "gemm_i8.hip", "dq8ca_q4.hip", "probe.hip",
-           "w8a16_gemm.hip", "calib.hip"]
+           "w8a16_gemm.hip", "calib.hip", "gptq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -16,6 +16,7 @@
 #include "calib.h"
 #include "dq8ca_q4.h"
 #include "gemm_i8.h"
+#include "gptq.h"
 #include "quant.h"
 #include "w8a16.h"
 #include "measure.h"
@@ -139,10 +140,13 @@ int aql_version(void) { return 100; }
 const char *aql_last_error(void) { return g_err.c_str(); }
 
 size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-  (void)N;
   if (M < 0 || N < 0 || K < 0) return 0;
   if (op == AQL_OP_Q8TA_Q8CSW) return ws_q8ta(M, K);
   if (op == AQL_OP_DQ8CA) return ws_dq8ca(M, K);
+  if (op == AQL_OP_GPTQ_INT8) {
+    if (M < 1 || M > aql::kGptqMaxBlock || K > AQL_MAX_K_INT8) return 0;
+    return aql::gptq_workspace_bytes(N, K, M);
+  }
   return 0;
 }
 
@@ -539,6 +543,32 @@ int aql_keep_outliers(const float *amax, const int32_t *seam, int64_t npoints, i
   }
   for (int32_t i = 0; i < nseams; ++i) keep[i] = seen[i] && worst[i] > factor * median;
   return ok();
+}
+
+int aql_gptq_int8(const float *w, int64_t N, int64_t K, const double *H, double damp,
+                  int64_t block, int8_t *q, float *scale, int32_t *wsum, double *hinv_out,
+                  int32_t *info, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "aql_gptq_int8";
+  REQUIRE(N >= 0 && K >= 4 && K % 4 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
+          "%s: need N >= 0, 4 <= K <= %d and K %% 4 == 0 (N=%lld K=%lld)", fn, AQL_MAX_K_INT8,
+          (long long)N, (long long)K);
+  REQUIRE(block >= 1 && block <= aql::kGptqMaxBlock, AQL_ERR_SHAPE,
+          "%s: block must be in 1..%d (got %lld)", fn, aql::kGptqMaxBlock, (long long)block);
+  REQUIRE(std::isfinite(damp) && damp >= 0.0, AQL_ERR_PARAM,
+          "%s: damp must be finite and >= 0", fn);
+  REQUIRE(aligned16(w) && aligned16(H) && aligned16(q) && aligned16(scale) && aligned16(wsum) &&
+              aligned16(hinv_out) && aligned16(info) && aligned16(ws),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (N == 0) return ok();
+  REQUIRE(w && H && q && scale && info, AQL_ERR_NULL,
+          "%s: w, H, q, scale and info must not be NULL", fn);
+  const size_t need = aql::gptq_workspace_bytes(N, K, block);
+  REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace of %zu bytes needed", fn,
+          need);
+  if (int e = check_device(fn)) return e;
+  return launched(aql::launch_gptq_int8(w, N, K, H, damp, (int)block, q, scale, wsum, hinv_out,
+                                        info, ws, (hipStream_t)stream),
+                  fn);
 }
 
 int aql_measure_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream) {

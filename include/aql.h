@@ -28,7 +28,8 @@
  * Citations name the page and the section that defines the operation:
  *   [SmolVLM q8 recipe]   SmolVLM-500M-Instruct ExecuTorch WebGPU 8-bit recipe
  *                         building blocks (module docstring, weight_int8,
- *                         fake_quant, Q8Linear, fix_q8ta_fake)
+ *                         fake_quant, Q8Linear, fix_q8ta_fake, act_observer,
+ *                         Recorder, calibrate, gptq_int8)
  *   [Ming INT8 linear]    Ming-Image-0.1-Design-ROCm-INT8 int8_linear
  *                         (QUANT_RULE, quantize_weight, Int8Linear)
  *   [tiny-llm quant]      tiny-llm quant module (Step 4.6 docstring,
@@ -69,6 +70,7 @@ extern "C" {
 
 #define AQL_OP_Q8TA_Q8CSW 1 /* workspace of aql_linear_q8ta_q8csw */
 #define AQL_OP_DQ8CA 2      /* workspace of aql_linear_dq8ca */
+#define AQL_OP_GPTQ_INT8 3  /* workspace of aql_gptq_int8 (M = the column block) */
 
 /* Largest K accepted by the int8 paths: keeps |sum_k (xq - z) q| below 2^31. */
 #define AQL_MAX_K_INT8 65536
@@ -352,6 +354,50 @@ int aql_minmax_observe(const float *x, int64_t rows, int64_t cols, int64_t seq, 
 int aql_minmax_qparams(const float *state, float *scale, int32_t *zp, void *stream);
 int aql_keep_outliers(const float *amax, const int32_t *seam, int64_t npoints, int32_t nseams,
                       double factor, int32_t *keep);
+
+/* ------------------------------------------------------------- GPTQ int8 */
+
+/*
+ * GPTQ codes for the int8 weight grid ([SmolVLM q8 recipe] gptq_int8, after
+ * Frantar et al.), in binary64, on the device. The scales are the weight
+ * quantizer's (AQL_WQ_SYM127_5 of the original w: amax / 127.5, fp32); the
+ * codes replace its rounding to nearest:
+ *   dead = (H[k][k] == 0): H[k][k] = 1 and weight column k zeroed;
+ *   Hd = H + damp * mean(diag H) * I;  hinv = chol(Hd^-1)^T (upper);
+ *   for each block of `block` columns, for each column i in order:
+ *     q[:, i] = clamp(round(w[:, i] / s), -128, 127),
+ *     e = (w[:, i] - q[:, i] s) / hinv[i][i],
+ *     w[:, j] -= e hinv[i][j] for the block's later columns j;
+ *   after the block, w[:, j] -= sum_t e_t hinv[t][j] for every later column j.
+ * The page leaves the order of its library reductions to LAPACK/BLAS. Here
+ * every sum (an element of a Cholesky factor, of the triangular inverse, of
+ * the product forming Hd^-1, of a block's trailing update, the diagonal's
+ * mean) is an ascending sum from 0, each product and addition rounded on its
+ * own, used once complete; fp64 division and square root correctly rounded,
+ * round half to even. Results are therefore reproducible bit for bit.
+ *
+ *   w         device, [N, K] float32
+ *   H         device, [K, K] float64, symmetric; only the lower triangle and
+ *             the diagonal are read
+ *   damp      relative damping (the page's default 0.01), finite and >= 0
+ *   block     columns per block, 1..256 (the page's default 128)
+ *   q         device, [N, K] int8 codes (output)
+ *   scale     device, [N] float32 (output)
+ *   wsum      device, [N] int32 sums of the codes (output; may be NULL)
+ *   hinv_out  device, [K, K] float64 (output; may be NULL): the upper factor,
+ *             zero below the diagonal
+ *   info      device, int32 (output): 0 on success; c (1-based) if pivot c of
+ *             the factor of Hd was not positive; K + c if pivot c of the factor
+ *             of Hd^-1 was not. Outputs are meaningless when info != 0.
+ *   ws        device workspace of aql_workspace_bytes(AQL_OP_GPTQ_INT8, block, N, K)
+ *             bytes (about 32 K^2 + 8 N K + 8 N block)
+ * Errors: N < 0; K < 4, K % 4 != 0 or K > AQL_MAX_K_INT8; block outside
+ * 1..256; damp not finite or negative; NULL or misaligned pointers; workspace
+ * too small. N == 0 launches nothing.
+ */
+int aql_gptq_int8(const float *w, int64_t N, int64_t K, const double *H, double damp,
+                  int64_t block, int8_t *q, float *scale, int32_t *wsum, double *hinv_out,
+                  int32_t *info, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------- measurement helpers */
 

@@ -45,6 +45,10 @@ def test_workspace_bytes():
     assert aql.aql_workspace_bytes(aql.AQL_OP_DQ8CA, 4, 11008, 4096) >= 4 * 4096 + 8 * 4
     assert aql.aql_workspace_bytes(99, 1, 1, 16) == 0
     assert aql.aql_workspace_bytes(aql.AQL_OP_DQ8CA, -1, 1, 16) == 0
+    g = aql.aql_workspace_bytes(aql.AQL_OP_GPTQ_INT8, 128, 4096, 4096)
+    assert g >= 4 * 8 * 4096 * 4096 + 8 * 4096 * 4096 + 8 * 4096 * 128 + 4096
+    assert aql.aql_workspace_bytes(aql.AQL_OP_GPTQ_INT8, 0, 16, 16) == 0       # block 0
+    assert aql.aql_workspace_bytes(aql.AQL_OP_GPTQ_INT8, 257, 16, 16) == 0     # block > 256
 
 
 def qw(*a):
@@ -187,6 +191,27 @@ def test_calibration_validation():
     assert k(amax, seam, -1, 2, 20.0, keep) == aql.AQL_ERR_SHAPE
     assert k(NUL, seam, 2, 2, 20.0, keep) == aql.AQL_ERR_NULL
     assert k(NUL, NUL, 0, 0, 20.0, NUL) == aql.AQL_OK
+
+
+def test_gptq_validation():
+    gq = L.aql_gptq_int8
+    big = 1 << 40
+    W = C.c_void_p(0x50000)
+    I = C.c_void_p(0x60000)
+    # (w, N, K, H, damp, block, q, scale, wsum, hinv, info, ws, ws_bytes, stream)
+    assert gq(A, 4, 6, B, 0.01, 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_SHAPE   # K % 4
+    assert gq(A, 4, 0, B, 0.01, 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_SHAPE
+    assert gq(A, -1, 8, B, 0.01, 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_SHAPE
+    assert gq(A, 4, 8, B, 0.01, 0, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_SHAPE
+    assert gq(A, 4, 8, B, 0.01, 257, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_SHAPE
+    assert gq(A, 4, 8, B, -0.5, 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_PARAM
+    assert gq(A, 4, 8, B, float("nan"), 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_PARAM
+    assert gq(A, 4, 8, NUL, 0.01, 128, Y, Y, NUL, NUL, I, W, big, None) == aql.AQL_ERR_NULL
+    assert gq(A, 4, 8, B, 0.01, 128, Y, Y, NUL, NUL, NUL, W, big, None) == aql.AQL_ERR_NULL  # info
+    assert gq(A, 4, 8, B, 0.01, 128, Y, Y, NUL, MIS, I, W, big, None) == aql.AQL_ERR_ALIGN
+    assert gq(A, 4, 8, B, 0.01, 128, Y, Y, NUL, NUL, I, W, 64, None) == aql.AQL_ERR_WORKSPACE
+    assert gq(A, 4, 8, B, 0.01, 128, Y, Y, NUL, NUL, I, NUL, big, None) == aql.AQL_ERR_WORKSPACE
+    assert gq(NUL, 0, 8, NUL, 0.01, 128, NUL, NUL, NUL, NUL, NUL, NUL, 0, None) == aql.AQL_OK
 
 
 def test_keep_outliers_matches_oracle():

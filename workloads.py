@@ -21,6 +21,13 @@ and distributions follow the decoder layers the pages quantize:
                 +-U(2500, 3500), random sign); W [4096, 4096] ~ N(0, 0.02);
                 rows 1..511 are the calibration rows.
   * dyn8da4w:   x [M, 4096] ~ N(0, 1), W [11008, 4096] ~ N(0, 0.02).
+  * gptq:       a SmolVLM-500M MLP weight W [N, K] ~ N(0, 0.02) with 1% outlier
+                rows, and a synthetic symmetric positive (semi)definite K x K
+                float64 matrix standing in for the Hessian of the layer's
+                calibration inputs: the Gram matrix Z^T Z of Z [S, K] whose
+                columns have log-uniform scales in [0.1, 10] and share 16
+                random latent factors (so the matrix is far from diagonal), with
+                chosen columns of Z set to zero (dead channels).
 """
 import numpy as np
 import torch
@@ -119,3 +126,19 @@ def dyn8da4w(M, seed=0, K=DYN_K, N=DYN_N):
 
 def small_matrix(g, rows, cols, std=1.0):
     return randn(g, rows, cols, std=std)
+
+
+def gptq(K, N, samples=None, seed=0, dead=()):
+    """Weight [N, K] float32 and a synthetic Hessian stand-in [K, K] float64."""
+    g = gen(seed)
+    w = randn(g, N, K, std=0.02)
+    outlier_rows(g, w)
+    S = samples if samples is not None else 2 * K
+    scale = torch.exp(torch.empty(K).uniform_(np.log(0.1), np.log(10.0), generator=g))
+    factors = randn(g, S, 16) @ randn(g, 16, K)
+    z = (randn(g, S, K) + 0.5 * factors) * scale
+    z = z.double()
+    for d in dead:
+        z[:, d] = 0.0
+    H = (z.T @ z).numpy()
+    return {"w": w, "H": np.ascontiguousarray(H)}

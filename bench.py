@@ -47,6 +47,7 @@ METRIC = "W8A16 decode GEMV GB/s (% HBM peak); W8A8 prefill GEMM TOPS (% int8 MF
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP64_PEAK_TFLOPS = 78.6      # MI355X fp64 vector (fused multiply-add counted as 2)
 MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = "k_w8a16_m1_grouped_smolvlm_decode_sweep_traffic.md"
@@ -65,7 +66,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline")
     ap.add_argument("--only", default=None,
-                    help="profile helper: run just one workload (sweep|llm7b|q8ta|dq8ca|quant|calib|copy)")
+                    help="profile helper: run just one workload "
+                         "(sweep|llm7b|q8ta|dq8ca|quant|calib|gptq|copy)")
     ap.add_argument("--no-settle", action="store_true",
                     help="profile helper: skip the settle phase (counter runs serialize every "
                          "dispatch, so settling there only costs time)")
@@ -375,6 +377,52 @@ def sec_calib(torch, aql, workloads, dev):
     return out
 
 
+def gptq_flops(N, K, block):
+    """Algorithmic fp64 operations of GPTQ int8 (one multiply and one add per
+    term): the two Cholesky factors, the triangular inverse and the product
+    forming H^-1 (K^3/3 each), and the column loop (per row: the block's
+    in-block updates and every block's trailing update)."""
+    fact = 4.0 * K ** 3 / 3.0
+    loop = 0.0
+    for i1 in range(0, K, block):
+        bl = min(block, K - i1)
+        loop += bl * (bl - 1) / 2.0 + bl * (K - i1 - bl)
+    return fact + 2.0 * N * loop
+
+
+def sec_gptq(torch, aql, workloads, dev):
+    """GPTQ int8 (binary64, bit-exact with the oracle) of a SmolVLM-500M MLP on
+    a synthetic Hessian: up and gate share their input, so they run as one
+    call on [5120, 960]; down is [960, 2560]. Plus a 4096 x 4096 layer."""
+    out = []
+    for name, K, N in (("smolvlm up+gate", 960, 5120), ("smolvlm down", 2560, 960),
+                       ("4096x4096", 4096, 4096)):
+        d = workloads.gptq(K, N, seed=9)
+        w = d["w"].to(dev)
+        H = torch.from_numpy(d["H"]).to(dev)
+        ws = torch.empty(aql.aql_workspace_bytes(aql.AQL_OP_GPTQ_INT8, 128, N, K),
+                         dtype=torch.uint8, device=dev)
+        q = torch.empty(N, K, dtype=torch.int8, device=dev)
+        s = torch.empty(N, dtype=torch.float32, device=dev)
+        wsum = torch.empty(N, dtype=torch.int32, device=dev)
+        info = torch.empty(1, dtype=torch.int32, device=dev)
+        fn = lambda i: aql.aql_gptq_int8(w, H, 0.01, 128, q, s, wsum, False, info, ws)
+        fn(0)
+        torch.cuda.synchronize()
+        if int(info.cpu()[0]) != 0:
+            raise RuntimeError(f"gptq {name}: info {int(info.cpu()[0])}")
+        med, _ = event_time_ms(torch, fn, 3, 1, trials=3)
+        fl = gptq_flops(N, K, 128)
+        row = {"workload": f"gptq_int8 {name} K={K} N={N} block=128 (fp64)", "ms": med,
+               "TFLOP/s": fl / (med * 1e-3) / 1e12,
+               "frac_fp64": fl / (med * 1e-3) / 1e12 / FP64_PEAK_TFLOPS}
+        say(row)
+        out.append(row)
+        del ws, w, H
+        torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline
 
 
@@ -497,7 +545,7 @@ def main():
     secondary = []
     if args.only is not None and args.only != "sweep":
         fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant,
-              "calib": sec_calib, "copy": sec_copy}[args.only]
+              "calib": sec_calib, "copy": sec_copy, "gptq": sec_gptq}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
         return
     calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)
@@ -507,7 +555,7 @@ def main():
     del calls
     torch.cuda.empty_cache()
     if args.only is None and not args.no_secondary:
-        for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant, sec_calib):
+        for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant, sec_calib, sec_gptq):
             secondary += fn(torch, aql, workloads, dev)
             torch.cuda.empty_cache()
 

@@ -42,7 +42,6 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int PB = 32;        // panel width of the factorizations
 constexpr int SB = 128;       // columns whose trailing update is applied at once
-constexpr int LDD = PB + 2;   // LDS row of a diagonal block (16-byte aligned)
 constexpr int TKC = 16;       // k_seqdot: k per LDS stage
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -158,29 +157,35 @@ __global__ __launch_bounds__(256) void k_gptq_upper_of(const double *__restrict_
 
 // -------------------------------------------------------- panel kernels
 
-// One 32-column panel [k0, k0 + bn) of the lower Cholesky factor L of A.
-// acc[i][j] holds sum_{k < k0} L[i][k] L[j][k] (ascending k) from the earlier
-// panels' updates. Every workgroup factors the diagonal block in LDS (thread t
-// owns row t; element (t, j) completes its sum at step j); workgroup 0 stores
-// it, workgroup g >= 1 then solves rows k0 + 32 + 64 (g - 1) .. + 63 of the
-// panel, one thread a row, the row held in registers. Past the matrix the block
-// is padded with an identity, which keeps the padded pivots at 1.
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_chol_panel(const double *__restrict__ A,
-                                                   const double *__restrict__ acc,
-                                                   double *__restrict__ L, int64_t K, int64_t k0,
-                                                   int32_t *info, int32_t code0) {
-  __shared__ __attribute__((aligned(16))) double D[PB][LDD];  // diagonal block of L
-  __shared__ double Da[PB][PB + 1];                           // ... of A
-  __shared__ double Dc[PB][PB + 1];                           // ... of acc
-  __shared__ double R[PB][65];  // [col][row]: this workgroup's rows of A, then of L
-  __shared__ double S[PB][65];  // [col][row]: their partial sums
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// One 32-column panel [k0, k0 + bn) of the lower Cholesky factor L of A, in
+// one wave. acc[i][j] holds sum_{k < k0} L[i][k] L[j][k] (ascending k) from the
+// earlier panels' updates. Every workgroup factors the diagonal block (lane t
+// holds row t); workgroup 0 stores it, workgroup g >= 1 then solves rows
+// k0 + 32 + 64 (g - 1) .. + 63 of the panel (lane t, row t). Both are
+// right-looking: at step k the new column k of L (lane j's value, read with
+// readlane) adds its term k to every later element's running sum, so each sum
+// still runs over k in ascending order. Past the matrix the diagonal block is
+// padded with an identity, which keeps the padded pivots at 1.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_chol_panel(
+    const double *__restrict__ A, const double *__restrict__ acc, double *__restrict__ L,
+    int64_t K, int64_t k0, int32_t *info, int32_t code0) {
+  __shared__ double Da[PB][PB + 1];  // diagonal block of A (row-major)
+  __shared__ double Dc[PB][PB + 1];  // ... of acc
+  __shared__ double R[64][PB + 1];   // this workgroup's rows of A
+  __shared__ double S[64][PB + 1];   // ... of acc
   const int t = threadIdx.x, tr = t & (PB - 1);
   const int bn = (int)(K - k0 < PB ? K - k0 : PB);
   constexpr int DM = PB * PB / 64;  // diagonal-block elements a thread stages
   const int64_t r0 = k0 + PB + (int64_t)(blockIdx.x - 1) * 64;
   {
-    // all loads first, then the LDS writes
-    // (the selects come after all the loads: the unrolled code keeps source order)
+    // all loads first, then the selects (the unrolled code keeps source order)
     double va[DM], vc[DM];
 #pragma unroll
     for (int m = 0; m < DM; ++m) {
@@ -205,101 +210,91 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       const bool ok = r < bn && tr <= r;
       Da[r][tr] = ok ? va[m] : (r == tr ? 1.0 : 0.0);
       Dc[r][tr] = ok ? vc[m] : 0.0;
-      D[r][tr] = 0.0;
     }
     if (blockIdx.x > 0) {
 #pragma unroll
       for (int m = 0; m < PB; ++m) {
         const int r = m * (64 / PB) + t / PB;
         const bool ok = r0 + r < K;
-        R[tr][r] = ok ? ra[m] : 0.0;
-        S[tr][r] = ok ? rc[m] : 0.0;
+        R[r][tr] = ok ? ra[m] : 0.0;
+        S[r][tr] = ok ? rc[m] : 0.0;
       }
     }
   }
   __syncthreads();
-  double lr[PB];
+
+  // diagonal block: lane t (and t + 32, a copy) holds row tr; sd[j] is the
+  // running sum of element (tr, j)
+  double sd[PB], lr[PB];
 #pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    double a = Dc[tr][j];
+  for (int j = 0; j < PB; ++j) sd[j] = Dc[tr][j];
 #pragma unroll
-    for (int k = 0; k < j; ++k) a = a + lr[k] * D[j][k];
-    if (t == j) {
-      const double d = Da[j][j] - a;
-      if (info && j < bn && !(d > 0.0)) atomicCAS(info, 0, code0 + j + 1);
-      D[j][j] = sqrt(d);
-    }
-    __syncthreads();
-    const double ljj = D[j][j];
-    const double l = (Da[tr][j] - a) / ljj;
-    lr[j] = t == j ? ljj : l;
-    if (t > j && t < PB) D[t][j] = l;
-    __syncthreads();
+  for (int k = 0; k < PB; ++k) {
+    const double d = readlane_f64(Da[tr][k], k) - readlane_f64(sd[k], k);
+    if (info && t == 0 && k < bn && !(d > 0.0)) atomicCAS(info, 0, code0 + k + 1);
+    const double lkk = sqrt(d);
+    const double l = tr == k ? lkk : (Da[tr][k] - sd[k]) / lkk;
+    lr[k] = l;
+#pragma unroll
+    for (int j = k + 1; j < PB; ++j) sd[j] = sd[j] + l * readlane_f64(l, j);
   }
   if (blockIdx.x == 0) {
-    for (int r = t / PB; r < bn; r += 64 / PB)
-      if (tr < bn) L[(k0 + r) * K + k0 + tr] = tr <= r ? D[r][tr] : 0.0;
+    if (t < bn) {
+#pragma unroll
+      for (int c = 0; c < PB; ++c)
+        if (c < bn) L[(k0 + t) * K + k0 + c] = c <= t ? lr[c] : 0.0;
+    }
     return;
   }
+
+  // rows below: lane t holds row r0 + t; lr[k] of lane j is L[k0 + j][k0 + k]
+  double sr[PB];
 #pragma unroll
-  for (int j = 0; j < PB; ++j) {
-    double a = S[j][t];
+  for (int j = 0; j < PB; ++j) sr[j] = S[t][j];
+  const int64_t row = r0 + t;
 #pragma unroll
-    for (int k = 0; k < j; ++k) a = a + lr[k] * D[j][k];
-    lr[j] = (R[j][t] - a) / D[j][j];
+  for (int k = 0; k < PB; ++k) {
+    const double l = (R[t][k] - sr[k]) / readlane_f64(lr[k], k);
+    if (row < K) L[row * K + k0 + k] = l;
+#pragma unroll
+    for (int j = k + 1; j < PB; ++j) sr[j] = sr[j] + l * readlane_f64(lr[k], j);
   }
-#pragma unroll
-  for (int j = 0; j < PB; ++j) R[j][t] = lr[j];
-  __syncthreads();
-  for (int r = t / PB; r < 64; r += 64 / PB)
-    if (r0 + r < K) L[(r0 + r) * K + k0 + tr] = R[tr][r];
 }
 
-// Rows [k0, k0 + bn) of Xm = L^-1, one thread a column j < k0 + bn:
+// Rows [k0, k0 + bn) of Xm = L^-1, one lane a column j < k0 + bn:
 // Xm[i][j] = 1 / L[i][i] (i == j), -(sum_{k=j}^{i-1} L[i][k] Xm[k][j]) / L[i][i]
 // (i > j), 0 (i < j). acc[i][j] holds the sum over k < k0 (the terms with k < j
-// are zero). Stored transposed: X[j][i] = Xm[i][j].
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_trinv_panel(const double *__restrict__ L,
-                                                    const double *__restrict__ acc,
-                                                    double *__restrict__ X, int64_t K,
-                                                    int64_t k0) {
-  __shared__ __attribute__((aligned(16))) double D[PB][LDD];  // L's diagonal block
-  __shared__ double V[PB][65];                                // [i][t]: Xm[k0 + i][j]
+// are zero). Right-looking: Xm[k][j] adds its term to rows i > k at step k.
+// Lane r (and r + 32) holds row r of L's diagonal block, read with readlane.
+// Stored transposed: X[j][i] = Xm[i][j].
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_trinv_panel(
+    const double *__restrict__ L, const double *__restrict__ acc, double *__restrict__ X,
+    int64_t K, int64_t k0) {
+  __shared__ double V[PB][65];  // [i][t]: Xm[k0 + i][j]
   const int t = threadIdx.x, tr = t & (PB - 1);
   const int bn = (int)(K - k0 < PB ? K - k0 : PB);
   const int64_t k1 = k0 + bn;
   const int64_t jb = (int64_t)blockIdx.x * 64, j = jb + t;
-  constexpr int DM = PB * PB / 64;
-  // staged diagonal block and this column's partial sums: all loads first (the
-  // unrolled code keeps source order), then the selects
-  double vd[DM], sv[PB];
+  // row tr of the diagonal block (identity past the matrix) and this column's
+  // partial sums: all loads first (the unrolled code keeps source order)
+  double ld[PB], sv[PB];
 #pragma unroll
-  for (int m = 0; m < DM; ++m) {
-    const int r = m * (64 / PB) + t / PB;
-    vd[m] = L[r < bn && tr <= r ? (k0 + r) * K + k0 + tr : 0];
-  }
+  for (int c = 0; c < PB; ++c) ld[c] = L[tr < bn && c <= tr ? (k0 + tr) * K + k0 + c : 0];
 #pragma unroll
   for (int r = 0; r < PB; ++r) sv[r] = acc[r < bn && j < k1 ? (k0 + r) * K + j : 0];
 #pragma unroll
-  for (int m = 0; m < DM; ++m) {
-    const int r = m * (64 / PB) + t / PB;
-    D[r][tr] = r < bn && tr <= r ? vd[m] : (r == tr ? 1.0 : 0.0);
-  }
+  for (int c = 0; c < PB; ++c) ld[c] = tr < bn && c <= tr ? ld[c] : (c == tr ? 1.0 : 0.0);
 #pragma unroll
   for (int r = 0; r < PB; ++r) sv[r] = r < bn && j < k1 ? sv[r] : 0.0;
-  __syncthreads();
-  double x[PB];
 #pragma unroll
   for (int i = 0; i < PB; ++i) {
     const int64_t gi = k0 + i;
-    double a = sv[i];
+    const double v = (gi == j ? 1.0 : -sv[i]) / readlane_f64(ld[i], i);
+    const double x = gi < j ? 0.0 : v;
+    V[i][t] = x;
 #pragma unroll
-    for (int k = 0; k < i; ++k) a = a + D[i][k] * x[k];
-    const double v = (gi == j ? 1.0 : -a) / D[i][i];
-    x[i] = gi < j ? 0.0 : v;
+    for (int r = i + 1; r < PB; ++r) sv[r] = sv[r] + readlane_f64(ld[i], r) * x;
   }
-#pragma unroll
-  for (int i = 0; i < PB; ++i) V[i][t] = x[i];
   __syncthreads();
   for (int r = t / PB; r < 64; r += 64 / PB)
     if (jb + r < k1 && tr < bn) X[(jb + r) * K + k0 + tr] = V[tr][r];
@@ -329,7 +324,10 @@ __global__ __launch_bounds__(256, 2) void k_seqdot(const double *__restrict__ P,
   constexpr int EP = TM / 16, EQ = TN / 16;   // k values a thread stages per row
   __shared__ __attribute__((aligned(16))) double Ps[2][TKC][TM + 2];
   __shared__ __attribute__((aligned(16))) double Qs[2][TKC][TN + 2];
-  const int64_t ti = i0 + (int64_t)blockIdx.x * TM, tj = j0 + (int64_t)blockIdx.y * TN;
+  // KFROM_ROW tiles get the row tile from blockIdx.y, so that the tiles with
+  // the longest sums (the first rows) are dispatched first.
+  const int64_t bx = KFROM_ROW ? blockIdx.y : blockIdx.x, by = KFROM_ROW ? blockIdx.x : blockIdx.y;
+  const int64_t ti = i0 + bx * TM, tj = j0 + by * TN;
   if (LOWER && tj > ti + TM - 1) return;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int64_t ks = KFROM_ROW ? (ti > kb ? ti : kb) : kb;
@@ -448,8 +446,9 @@ template <int MODE, bool LOWER, bool KFROM_ROW, int TI, int TJ>
 void seqdot_launch(const double *P, int64_t ldp, const double *Q, int64_t ldq, double *out,
                    int64_t ldo, int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t kb,
                    int64_t ke, hipStream_t st) {
-  const dim3 grid((unsigned)((i1 - i0 + 16 * TI - 1) / (16 * TI)),
-                  (unsigned)((j1 - j0 + 16 * TJ - 1) / (16 * TJ)));
+  const unsigned gr = (unsigned)((i1 - i0 + 16 * TI - 1) / (16 * TI));
+  const unsigned gc = (unsigned)((j1 - j0 + 16 * TJ - 1) / (16 * TJ));
+  const dim3 grid(KFROM_ROW ? gc : gr, KFROM_ROW ? gr : gc);
   k_seqdot<MODE, LOWER, KFROM_ROW, TI, TJ>
       <<<grid, 256, 0, st>>>(P, ldp, Q, ldq, out, ldo, i0, i1, j0, j1, kb, ke);
 }
@@ -481,12 +480,6 @@ void seqdot(const double *P, int64_t ldp, const double *Q, int64_t ldq, double *
 
 // ---------------------------------------------------------- column blocks
 
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
 
 // Columns [i1, i1 + bl) of every row, in order: qc = clamp(round(w / s), -128, 127),
 // e = (w - qc s) / hinv[i][i], then w[j] -= e hinv[i][j] for the block's later
@@ -639,7 +632,9 @@ hipError_t launch_gptq_int8(const float *w, int64_t N, int64_t K, const double *
   cholesky(b.A, b.acc, b.L, K, info, 0, st);
   k_fill_f64<<<fill_grid, 256, 0, st>>>(b.X, kk);
   tri_inverse(b.L, b.acc, b.X, K, st);
-  seqdot<SEQ_STORE, true, true>(b.X, K, b.X, K, b.A, K, 0, K, 0, K, 0, K, st);
+  // 64 x 64 tiles: the sums of the first tile row run over all of K, the last
+  // over one tile, so many small tiles (longest first) balance the chip
+  seqdot_launch<SEQ_STORE, true, true, 4, 4>(b.X, K, b.X, K, b.A, K, 0, K, 0, K, 0, K, st);
   cholesky(b.A, b.acc, b.L, K, info, (int32_t)K, st);
   // hinv = L^T (upper), into X
   k_gptq_upper_of<<<dim3((unsigned)((K + 63) / 64), (unsigned)((K + 63) / 64)), 256, 0, st>>>(

@@ -315,8 +315,11 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   const bool m1 = h->mblocks == 0;
   REQUIRE(h->magic == kGroupMagic && h->version == 2 && h->count >= 0 && h->total_blocks >= 0 &&
               (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8) &&
-              (h->mblocks == 0 || h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4) &&
-              (h->tgroups == 1 || h->tgroups == 2 || h->tgroups == 4) &&
+              (h->mblocks == 0 || h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4 ||
+               h->mblocks == aql::kW8A16Skinny) &&
+              (h->mblocks == aql::kW8A16Skinny ? (h->tgroups == 4 || h->tgroups == 8)
+                                               : (h->tgroups == 1 || h->tgroups == 2 ||
+                                                  h->tgroups == 4)) &&
               (m1 ? (h->tgroups == 2 && (h->cgroups == 1 || h->cgroups == 2 || h->cgroups == 4) &&
                      h->waves * h->cgroups <= 16 && h->xlds >= 0 &&
                      h->xlds <= aql::kW8A16MaxXlds && h->xlds % 1024 == 0)

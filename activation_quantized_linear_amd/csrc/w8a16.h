@@ -13,7 +13,9 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
 
 // Launch shape of the W8A16 kernel: waves per channel group (they split K),
 // groups of 4 output channels per wave tile (1, 2 or 4) and blocks of 4 rows of
-// x per tile (1, 2 or 4; 0 selects the single-row tile, M = 1). The single-row
+// x per tile (1, 2 or 4; 0 selects the single-row tile, M = 1; kW8A16Skinny
+// selects the 16-row skinny tile on 16x16x32 MFMAs, with 4 or 8 channel
+// groups). The single-row
 // tile also takes cgroups, wave tiles along N per workgroup (1, 2 or 4), and
 // xlds, the LDS bytes the workgroup copies x into (0: each wave loads its x
 // from memory; else 2 K rounded up to 1 KiB for the largest K it serves).
@@ -23,6 +25,8 @@ struct W8A16Shape {
   int xlds = 0;
 };
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K);
+constexpr int kW8A16Skinny = 16;     // mblocks value of the skinny tile
+constexpr int kW8A16SkinnyMinM = 9;  // rows from which the skinny tile serves (up to the GEMM band)
 // LDS budget for x in the single-row tile (K <= 16384), and the xlds value for
 // a given K (0 past the budget).
 constexpr int kW8A16MaxXlds = 32768;

@@ -347,6 +347,116 @@ __device__ __forceinline__ void w8a16_tile(const Tile &t, Red<W, TG, MB> &red) {
   }
 }
 
+// Skinny tile for 2 <= M <= 16 (16 rows of x, 16 NT channels): one
+// v_mfma_f32_16x16x32_bf16 per 32 k and 16 channels, x as the A operand (row
+// m = lane % 16), the widened int8 weights as B (channel n = lane % 16), so a
+// lane keeps one 16 x 16 accumulator tile per 16 channels instead of the
+// 4 x 4 x 4 tile's 16 k-slice partials, and each matrix instruction does 8x
+// the work. The k order inside a step is free as long as x and the weights
+// use the same one: lane group g = lane / 16 of instruction (h, half) takes
+// k = 256 step + 64 h + 16 g + 8 half + e (e = 0..7), so a lane's weight
+// load is 16 contiguous bytes of its channel's row (both halves) and its x
+// loads are 32 contiguous bytes of its row. W waves split K into 256-byte
+// steps as in the 4 x 4 tile; batches of U steps are double-buffered.
+template <int W, int NT, int U>
+__device__ __forceinline__ void w8a16_tile_sk(const Tile &t, f32x4 (*red)[NT][64]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t K = t.K;
+  const int64_t nrows = t.N - t.n0 < 16 * NT ? t.N - t.n0 : 16 * NT;
+  const int64_t mrows = t.M - t.m0 < 16 ? t.M - t.m0 : 16;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(t.q + t.n0 * K, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(t.x + t.m0 * K, (uint32_t)(mrows * K * 2));
+  const uint32_t qlane = (uint32_t)(r * K + 16 * g);       // channel r, bytes 16 g
+  const uint32_t xlane = 2u * (uint32_t)(r * K + 16 * g);  // row r, elements 16 g
+  const int nst = (int)((K + 255) >> 8);
+  const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one step: 4 NT weight loads (16 bytes of a channel row each), 8 x loads
+  auto fetch = [&](int i0, i32x4 (*w_)[NT][4], i32x4 (*x_)[4][2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      const int st = wave + W * i;
+      const bool valid = i < cnt;  // uniform
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        // this lane's 16 k of chunk h lie before K (only the last step can end early)
+        const bool kin = valid && (256 * st + 64 * h + 16 * g) < K;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+          const int qo = kin ? (int)(qlane + (uint32_t)(16 * c) * (uint32_t)K + 256u * st + 64u * h)
+                             : OOB;
+          w_[u][c][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
+        }
+        const int xo = kin ? (int)(xlane + 512u * st + 128u * h) : OOB;
+        x_[u][h][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+        x_[u][h][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, 0, 0);
+      }
+    }
+  };
+  auto mul = [&](i32x4 (*w_)[NT][4], i32x4 (*x_)[4][2]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, x_[u][h][half]);
+#pragma unroll
+          for (int c = 0; c < NT; ++c) {
+            const s16x4 lo = widen4(w_[u][c][h][2 * half]), hi = widen4(w_[u][c][h][2 * half + 1]);
+            const bf16x8 b = __builtin_bit_cast(
+                bf16x8, i32x4{(int)__builtin_bit_cast(i32x2, lo)[0], (int)__builtin_bit_cast(i32x2, lo)[1],
+                              (int)__builtin_bit_cast(i32x2, hi)[0], (int)__builtin_bit_cast(i32x2, hi)[1]});
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+          }
+        }
+  };
+
+  i32x4 w0[U][NT][4], w1[U][NT][4], x0[U][4][2], x1[U][4][2];
+  fetch(0, w0, x0);
+  for (int b = 0; b < cnt; b += 2 * U) {
+    fetch(b + U, w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(b + 2 * U, w0, x0);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(w1, x1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // waves meet in LDS; wave 0 lane l holds rows 4 g + v of channel 16 c + r
+  if constexpr (W > 1) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) red[wave][c][lane] = acc[c];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+      for (int w = 1; w < W; ++w) acc[c] += red[w][c][lane];
+  }
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const int64_t n = t.n0 + 16 * c + r;
+    if (n >= t.N) continue;
+    const float s = t.scale[n];
+    const float bv = t.bias ? bf16_to_f32(t.bias[n]) : 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mm = t.m0 + 4 * g + v;
+      if (mm < t.M) t.y[mm * t.N + n] = f32_to_bf16_rne(s * acc[c][v] + bv);
+    }
+  }
+}
+
 template <int TG, int MB>
 constexpr int batch_steps() {
   return TG * MB <= 8 ? 2 : 1;
@@ -389,6 +499,26 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_grouped(const W8A16GroupEntry 
                                                           int count) {
   __shared__ Red<W, TG, MB> red;
   w8a16_tile<W, TG, MB, batch_steps<TG, MB>()>(group_tile(tab, count, 4 * TG), red);
+}
+
+// Skinny tile (M <= 16): 16 NT channels x 16 rows per workgroup of W waves.
+template <int W, int NT>
+__global__ __launch_bounds__(64 * W) void k_w8a16_sk(const uint16_t *__restrict__ x, int64_t M,
+                                                     int64_t K, const int8_t *__restrict__ q,
+                                                     const float *__restrict__ scale,
+                                                     const uint16_t *__restrict__ bias, int64_t N,
+                                                     uint16_t *__restrict__ y) {
+  __shared__ f32x4 red[W][NT][64];
+  const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 16 * NT,
+               (int64_t)blockIdx.y * 16};
+  w8a16_tile_sk<W, NT, 1>(t, red);
+}
+
+template <int W, int NT>
+__global__ __launch_bounds__(64 * W) void k_w8a16_sk_grouped(const W8A16GroupEntry *__restrict__ tab,
+                                                             int count) {
+  __shared__ f32x4 red[W][NT][64];
+  w8a16_tile_sk<W, NT, 1>(group_tile(tab, count, 16 * NT), red);
 }
 
 // Single-row tile; dynamic LDS holds x when XL.
@@ -438,6 +568,42 @@ void launch_group(int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab,
     break;
     AQL_W(16) AQL_W(8) AQL_W(4) AQL_W(2) default : AQL_W(1)
 #undef AQL_W
+  }
+}
+
+template <int NT>
+void launch_sk_single(int W, dim3 grid, hipStream_t st, const uint16_t *x, int64_t M, int64_t K,
+                      const int8_t *q, const float *scale, const uint16_t *bias, int64_t N,
+                      uint16_t *y) {
+  switch (W) {
+#define AQL_W(w)                                                                              \
+  case w:                                                                                     \
+    hipLaunchKernelGGL((k_w8a16_sk<w, NT>), grid, dim3(64 * w), 0, st, x, M, K, q, scale, bias, \
+                       N, y);                                                                 \
+    break;
+    AQL_W(8) AQL_W(4) AQL_W(2) AQL_W(1)
+#undef AQL_W
+    default:  // 16 waves (32 channels would not fit the registers of 1024 threads)
+      hipLaunchKernelGGL((k_w8a16_sk<NT == 1 ? 16 : 8, NT>), grid, dim3(NT == 1 ? 1024 : 512), 0,
+                         st, x, M, K, q, scale, bias, N, y);
+      break;
+  }
+}
+
+template <int NT>
+void launch_sk_group(int W, int blocks, hipStream_t st, const W8A16GroupEntry *tab, int count) {
+  const dim3 grid((unsigned)blocks);
+  switch (W) {
+#define AQL_W(w)                                                                               \
+  case w:                                                                                      \
+    hipLaunchKernelGGL((k_w8a16_sk_grouped<w, NT>), grid, dim3(64 * w), 0, st, tab, count);     \
+    break;
+    AQL_W(8) AQL_W(4) AQL_W(2) AQL_W(1)
+#undef AQL_W
+    default:  // 16 waves
+      hipLaunchKernelGGL((k_w8a16_sk_grouped<NT == 1 ? 16 : 8, NT>), grid,
+                         dim3(NT == 1 ? 1024 : 512), 0, st, tab, count);
+      break;
   }
 }
 
@@ -498,9 +664,20 @@ bool m1_shape_ok(const W8A16Shape &sh) {
 // on smaller grids the halved workgroup count costs more than it saves.
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
   W8A16Shape s;
+  const int64_t nst = (K + 255) / 256;  // 256-byte K steps
+  if (M >= kW8A16SkinnyMinM) {
+    // skinny tile: 16 rows x 16 NT channels on 16x16x32 MFMAs
+    s.mblocks = kW8A16Skinny;
+    s.tgroups = N >= 8192 ? 8 : 4;
+    const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
+    int W = 1;
+    const int wmax = s.tgroups == 8 ? 8 : 16;  // 1024 threads leave too few registers for 32 channels
+    while (W < wmax && tiles * W < 1024 && W * 4 <= nst) W <<= 1;
+    s.waves = W;
+    return s;
+  }
   s.mblocks = M == 1 ? 0 : (M <= 4 ? 1 : (M <= 8 ? 2 : 4));
   s.tgroups = M <= 2 ? 2 : 4;
-  const int64_t nst = (K + 255) / 256;  // 256-byte K steps
   const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
   const int64_t want = M == 1 ? 3072 : 768;
   const int wmax = M == 1 ? 8 : 16;
@@ -534,6 +711,11 @@ hipError_t launch_w8a16_shape(const W8A16Shape &sh, const uint16_t *x, int64_t M
   }
   const int64_t rows = 4 * sh.tgroups;
   const dim3 grid((unsigned)((N + rows - 1) / rows), (unsigned)((M + 15) / 16));
+  if (sh.mblocks == kW8A16Skinny) {
+    if (sh.tgroups == 8) launch_sk_single<2>(sh.waves, grid, st, x, M, K, q, scale, bias, N, y);
+    else launch_sk_single<1>(sh.waves, grid, st, x, M, K, q, scale, bias, N, y);
+    return hipGetLastError();
+  }
   switch (sh.tgroups) {
     case 1: launch_single_tg<1>(sh.mblocks, sh.waves, grid, st, x, M, K, q, scale, bias, N, y); break;
     case 2: launch_single_tg<2>(sh.mblocks, sh.waves, grid, st, x, M, K, q, scale, bias, N, y); break;
@@ -558,6 +740,11 @@ hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int t
           (k_w8a16_m1_grouped<decltype(w)::value, decltype(c)::value, decltype(xl)::value>), grid,
           block, sh.xlds, st, dev_tab, count);
     });
+    return hipGetLastError();
+  }
+  if (sh.mblocks == kW8A16Skinny) {
+    if (sh.tgroups == 8) launch_sk_group<2>(sh.waves, total_blocks, st, dev_tab, count);
+    else launch_sk_group<1>(sh.waves, total_blocks, st, dev_tab, count);
     return hipGetLastError();
   }
   switch (sh.tgroups) {

@@ -232,6 +232,41 @@ def test_w8a16_shapes(M, N, K, with_bias):
     check_float(y, yref, tol, BF16, f"w8a16 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(9, 8200, 512), (12, 45, 4096), (31, 8195, 272),
+                                   (63, 100, 1040), (16, 32, 16), (10, 17, 14336)])
+def test_w8a16_skinny_tile(M, N, K):
+    """9 <= M < 64 runs the 16-row skinny tile on 16x16x32 MFMAs (32-channel
+    tiles from N = 8192): ragged channel and row tiles, one 16-k step, and a
+    K whose steps are split over the most waves."""
+    say("w8a16 skinny", M, N, K)
+    g = workloads.gen(900 + M + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+    b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16)
+    y, yref, tol = _w8a16_case(x, w, b)
+    check_float(y, yref, tol, BF16, f"w8a16 skinny {M}x{N}x{K}")
+
+
+def test_w8a16_grouped_skinny():
+    """A grouped launch whose largest M selects the skinny tile for every
+    problem (M from 1 to 40)."""
+    g = workloads.gen(910)
+    shapes = [(40, 300, 512), (1, 2560, 960), (9, 8200, 256), (16, 70, 4112)]
+    probs, refs = [], []
+    for M, N, K in shapes:
+        w = workloads.small_matrix(g, N, K, std=0.02)
+        x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+        q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        y = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        probs.append((dev(x), q, s, None, y))
+        refs.append(x)
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    aql.aql_linear_w8a16_grouped(host_t, dev_t)
+    for (x, q, s, _, y), xc in zip(probs, refs):
+        yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s), None)
+        check_float(host(y.float()), yref, tol, BF16, f"grouped skinny {tuple(y.shape)}")
+
+
 def test_w8a16_smolvlm_sweep():
     layers = workloads.smolvlm(seed=0)
     say("w8a16 smolvlm sweep", len(layers))

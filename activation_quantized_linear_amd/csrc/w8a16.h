@@ -26,7 +26,7 @@ struct W8A16Shape {
 };
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K);
 constexpr int kW8A16Skinny = 16;     // mblocks value of the skinny tile
-constexpr int kW8A16SkinnyMinM = 9;  // rows from which the skinny tile serves (up to the GEMM band)
+constexpr int kW8A16SkinnyMinM = 4;  // rows from which the skinny tile serves (up to the GEMM band)
 // LDS budget for x in the single-row tile (K <= 16384), and the xlds value for
 // a given K (0 past the budget).
 constexpr int kW8A16MaxXlds = 32768;

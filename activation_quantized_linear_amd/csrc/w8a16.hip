@@ -347,19 +347,37 @@ __device__ __forceinline__ void w8a16_tile(const Tile &t, Red<W, TG, MB> &red) {
   }
 }
 
-// Skinny tile for 2 <= M <= 16 (16 rows of x, 16 NT channels): one
-// v_mfma_f32_16x16x32_bf16 per 32 k and 16 channels, x as the A operand (row
-// m = lane % 16), the widened int8 weights as B (channel n = lane % 16), so a
-// lane keeps one 16 x 16 accumulator tile per 16 channels instead of the
-// 4 x 4 x 4 tile's 16 k-slice partials, and each matrix instruction does 8x
-// the work. The k order inside a step is free as long as x and the weights
-// use the same one: lane group g = lane / 16 of instruction (h, half) takes
-// k = 256 step + 64 h + 16 g + 8 half + e (e = 0..7), so a lane's weight
-// load is 16 contiguous bytes of its channel's row (both halves) and its x
-// loads are 32 contiguous bytes of its row. W waves split K into 256-byte
-// steps as in the 4 x 4 tile; batches of U steps are double-buffered.
-template <int W, int NT, int U>
-__device__ __forceinline__ void w8a16_tile_sk(const Tile &t, f32x4 (*red)[NT][64]) {
+// Skinny tile (16 rows of x, 16 NT channels): one v_mfma_f32_16x16x32_bf16
+// per 32 k and 16 channels, x as the A operand (row m = lane % 16), the
+// widened int8 weights as B (channel n = lane % 16), so a lane keeps one
+// 16 x 16 accumulator tile per 16 channels instead of the 4 x 4 x 4 tile's 16
+// k-slice partials, and each matrix instruction does 8x the work. The k order
+// inside a step is free as long as x and the weights use the same one: lane
+// group g = lane / 16 of instruction (h, half) takes k = 256 step + 64 h +
+// 16 g + 8 half + e (e = 0..7), so a lane reads 16 contiguous weight bytes of
+// its channel and 32 contiguous x bytes of its row.
+//
+// The weights arrive in the fast streaming shape, 4 rows x 256 bytes per wave
+// instruction, by buffer loads that write LDS directly, into a per-wave
+// double-buffered slot (no barrier: no other wave reads it); each 16-byte
+// chunk c of row r sits at slot c ^ (r % 16), so the MFMA-order reads of 16
+// rows hit distinct banks. x comes into registers. W waves split K into
+// 256-byte steps; the next step's loads are in flight while one is multiplied.
+template <int W, int NT>
+struct SkLds {
+  uint8_t w[W][2][16 * NT * 256];  // per wave, two step slots of 16 NT rows x 256 B
+  f32x4 red[W][NT][64];
+};
+
+// s_waitcnt vmcnt(N) with expcnt / lgkmcnt left at their maxima (N < 64).
+template <int N>
+__device__ __forceinline__ void sk_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int W, int NT>
+__device__ __forceinline__ void w8a16_tile_sk(const Tile &t, SkLds<W, NT> &sm) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -368,80 +386,96 @@ __device__ __forceinline__ void w8a16_tile_sk(const Tile &t, f32x4 (*red)[NT][64
   const int64_t mrows = t.M - t.m0 < 16 ? t.M - t.m0 : 16;
   const __amdgpu_buffer_rsrc_t rq = rsrc(t.q + t.n0 * K, (uint32_t)(nrows * K));
   const __amdgpu_buffer_rsrc_t rx = rsrc(t.x + t.m0 * K, (uint32_t)(mrows * K * 2));
-  const uint32_t qlane = (uint32_t)(r * K + 16 * g);       // channel r, bytes 16 g
-  const uint32_t xlane = 2u * (uint32_t)(r * K + 16 * g);  // row r, elements 16 g
   const int nst = (int)((K + 255) >> 8);
   const int cnt = wave < nst ? (nst - wave + W - 1) / W : 0;
+  // weight DMA: instruction i of a step covers rows 4 i .. 4 i + 3; lane l
+  // writes row 4 i + l / 16, slot l % 16 with chunk (l % 16) ^ (row % 16)
+  const int drow = lane >> 4, dslot = lane & 15;
+  const uint32_t xlane = 2u * (uint32_t)(r * K + 16 * g);  // row r, elements 16 g
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&sm.w[wave][0][0];
 
   f32x4 acc[NT];
 #pragma unroll
   for (int c = 0; c < NT; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one step: 4 NT weight loads (16 bytes of a channel row each), 8 x loads
-  auto fetch = [&](int i0, i32x4 (*w_)[NT][4], i32x4 (*x_)[4][2]) {
+  constexpr int NV = 4 * NT + 8;  // vector memory instructions per step
+  auto fetch = [&](int i, int slot, i32x4 (*x_)[2]) {
+    const int st = wave + W * i;
+    const bool valid = i < cnt;  // uniform
+    const __amdgpu_buffer_rsrc_t rqv = rq;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u;
-      const int st = wave + W * i;
-      const bool valid = i < cnt;  // uniform
+    for (int d = 0; d < 4 * NT; ++d) {
+      const int row = 4 * d + drow;
+      const int c = dslot ^ (row & 15);
+      const bool kin = valid && (256 * st + 16 * c) < K;
+      const int qo = kin ? (int)((uint32_t)row * (uint32_t)K + 256u * st + 16u * c) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rqv,
+          (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(lds0 + (uint32_t)slot * (16 * NT * 256) +
+                                                                 1024u * d),
+          16, qo, 0, 0, 0);
+    }
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        // this lane's 16 k of chunk h lie before K (only the last step can end early)
-        const bool kin = valid && (256 * st + 64 * h + 16 * g) < K;
+    for (int h = 0; h < 4; ++h) {
+      const bool kin = valid && (256 * st + 64 * h + 16 * g) < K;
+      const int xo = kin ? (int)(xlane + 512u * st + 128u * h) : OOB;
+      x_[h][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+      x_[h][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, 0, 0);
+    }
+  };
+  auto mul = [&](int slot, i32x4 (*x_)[2]) {
+    const uint8_t *wl = &sm.w[wave][slot][0];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      i32x4 wq[NT];
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        const int row = 16 * c + r;
+        wq[c] = *reinterpret_cast<const i32x4 *>(wl + 256 * row + 16 * ((4 * h + g) ^ r));
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, x_[h][half]);
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
-          const int qo = kin ? (int)(qlane + (uint32_t)(16 * c) * (uint32_t)K + 256u * st + 64u * h)
-                             : OOB;
-          w_[u][c][h] = __builtin_amdgcn_raw_buffer_load_b128(rq, qo, 0, 2);
+          const s16x4 lo = widen4(wq[c][2 * half]), hi = widen4(wq[c][2 * half + 1]);
+          const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, i32x4{l2[0], l2[1], h2[0], h2[1]});
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
         }
-        const int xo = kin ? (int)(xlane + 512u * st + 128u * h) : OOB;
-        x_[u][h][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
-        x_[u][h][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, xo + 16, 0, 0);
       }
     }
   };
-  auto mul = [&](i32x4 (*w_)[NT][4], i32x4 (*x_)[4][2]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, x_[u][h][half]);
-#pragma unroll
-          for (int c = 0; c < NT; ++c) {
-            const s16x4 lo = widen4(w_[u][c][h][2 * half]), hi = widen4(w_[u][c][h][2 * half + 1]);
-            const bf16x8 b = __builtin_bit_cast(
-                bf16x8, i32x4{(int)__builtin_bit_cast(i32x2, lo)[0], (int)__builtin_bit_cast(i32x2, lo)[1],
-                              (int)__builtin_bit_cast(i32x2, hi)[0], (int)__builtin_bit_cast(i32x2, hi)[1]});
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-          }
-        }
-  };
 
-  i32x4 w0[U][NT][4], w1[U][NT][4], x0[U][4][2], x1[U][4][2];
-  fetch(0, w0, x0);
-  for (int b = 0; b < cnt; b += 2 * U) {
-    fetch(b + U, w1, x1);
+  // Ping-pong over the two slots; a step past the wave's last loads zeros, so
+  // the loop needs no early exit. Before a step is read, everything but the
+  // following step's NV loads has landed (loads complete in order).
+  i32x4 x0[4][2], x1[4][2];
+  fetch(0, 0, x0);
+  for (int b = 0; b < cnt; b += 2) {
+    fetch(b + 1, 1, x1);
+    sk_wait_vm<NV>();
     __builtin_amdgcn_sched_barrier(0);
-    mul(w0, x0);
+    mul(0, x0);
     __builtin_amdgcn_sched_barrier(0);
-    fetch(b + 2 * U, w0, x0);
+    fetch(b + 2, 0, x0);
+    sk_wait_vm<NV>();
     __builtin_amdgcn_sched_barrier(0);
-    mul(w1, x1);
+    mul(1, x1);
     __builtin_amdgcn_sched_barrier(0);
   }
+  sk_wait_vm<0>();
 
   // waves meet in LDS; wave 0 lane l holds rows 4 g + v of channel 16 c + r
   if constexpr (W > 1) {
 #pragma unroll
-    for (int c = 0; c < NT; ++c) red[wave][c][lane] = acc[c];
+    for (int c = 0; c < NT; ++c) sm.red[wave][c][lane] = acc[c];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int c = 0; c < NT; ++c)
 #pragma unroll
-      for (int w = 1; w < W; ++w) acc[c] += red[w][c][lane];
+      for (int w = 1; w < W; ++w) acc[c] += sm.red[w][c][lane];
   }
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
@@ -508,17 +542,17 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_sk(const uint16_t *__restrict_
                                                      const float *__restrict__ scale,
                                                      const uint16_t *__restrict__ bias, int64_t N,
                                                      uint16_t *__restrict__ y) {
-  __shared__ f32x4 red[W][NT][64];
+  __shared__ __attribute__((aligned(16))) SkLds<W, NT> sm;
   const Tile t{x, q, scale, bias, y, M, N, K, (int64_t)blockIdx.x * 16 * NT,
                (int64_t)blockIdx.y * 16};
-  w8a16_tile_sk<W, NT, 1>(t, red);
+  w8a16_tile_sk<W, NT>(t, sm);
 }
 
 template <int W, int NT>
 __global__ __launch_bounds__(64 * W) void k_w8a16_sk_grouped(const W8A16GroupEntry *__restrict__ tab,
                                                              int count) {
-  __shared__ f32x4 red[W][NT][64];
-  w8a16_tile_sk<W, NT, 1>(group_tile(tab, count, 16 * NT), red);
+  __shared__ __attribute__((aligned(16))) SkLds<W, NT> sm;
+  w8a16_tile_sk<W, NT>(group_tile(tab, count, 16 * NT), sm);
 }
 
 // Single-row tile; dynamic LDS holds x when XL.
@@ -671,8 +705,10 @@ W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
     s.tgroups = N >= 8192 ? 8 : 4;
     const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
     int W = 1;
+    // waves split K while the grid holds fewer than ~1024 wave tiles and each
+    // wave keeps at least 8 steps (shorter loops pay their fill and drain)
     const int wmax = s.tgroups == 8 ? 8 : 16;  // 1024 threads leave too few registers for 32 channels
-    while (W < wmax && tiles * W < 1024 && W * 4 <= nst) W <<= 1;
+    while (W < wmax && tiles * W < 1024 && 16 * W <= nst) W <<= 1;
     s.waves = W;
     return s;
   }

@@ -233,11 +233,13 @@ def test_w8a16_shapes(M, N, K, with_bias):
 
 
 @pytest.mark.parametrize("M,N,K", [(9, 8200, 512), (12, 45, 4096), (31, 8195, 272),
-                                   (63, 100, 1040), (16, 32, 16), (10, 17, 14336)])
+                                   (63, 100, 1040), (16, 32, 16), (10, 17, 14336),
+                                   (4, 100, 272), (4, 8200, 1040), (4, 33, 16), (4, 7, 14352)])
 def test_w8a16_skinny_tile(M, N, K):
-    """9 <= M < 64 runs the 16-row skinny tile on 16x16x32 MFMAs (32-channel
-    tiles from N = 8192): ragged channel and row tiles, one 16-k step, and a
-    K whose steps are split over the most waves."""
+    """4 <= M < 64 runs the 16-row skinny tile on 16x16x32 MFMAs (32-channel
+    tiles from N = 8192): ragged channel and row tiles (M = 4 fills a quarter
+    of the 16 rows), one 16-k step, and a K whose steps are split over the
+    most waves."""
     say("w8a16 skinny", M, N, K)
     g = workloads.gen(900 + M + N + K)
     w = workloads.small_matrix(g, N, K, std=0.02)

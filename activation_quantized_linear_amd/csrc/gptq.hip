@@ -15,11 +15,11 @@
 // sum from 0 with each product and addition rounded on its own, subtracted or
 // used once complete. The kernels get parallelism from independent elements
 // only: a sum is never split or reassociated. The factorizations are blocked
-// right-looking ones (32-column panels, trailing updates gathered over 128
-// columns) that keep each element's partial sum
-// in an accumulator matrix between launches, so the order per element stays
-// ascending; the O(K^3) and O(N K^2) parts run in one tiled fp64 kernel
-// (k_seqdot: 128 x 128 tiles, 8 x 8 accumulators a thread, operands staged
+// right-looking ones (32-column panels, one wave each; trailing updates
+// gathered over 128 columns) that keep each element's partial sum in an
+// accumulator matrix between launches, so the order per element stays
+// ascending. The O(K^3) and O(N K^2) parts run in one tiled fp64 kernel
+// (k_seqdot: up to 128 x 128 tiles, up to 8 x 8 sums a thread, operands staged
 // through LDS). Zero products entering a sum (the structural zeros of the
 // triangular factors, padding past a range) leave it unchanged: an accumulator
 // that starts at +0 never becomes -0, and x + (+-0) = x for x != 0.

@@ -66,8 +66,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline")
     ap.add_argument("--only", default=None,
-                    help="profile helper: run just one workload "
-                         "(sweep|llm7b|q8ta|dq8ca|quant|calib|gptq|copy)")
+                    help="run just one workload (sweep|llm7b|q8ta|dq8ca|quant|calib|gptq|copy), or a "
+                         "measurement outside the default run (wsweep: working-set sweep; oracle: "
+                         "the CPU oracle at full size beside the GPU)")
     ap.add_argument("--no-settle", action="store_true",
                     help="profile helper: skip the settle phase (counter runs serialize every "
                          "dispatch, so settling there only costs time)")
@@ -423,6 +424,135 @@ def sec_gptq(torch, aql, workloads, dev):
     return out
 
 
+def sec_wsweep(torch, aql, workloads, dev):
+    """Working-set sweep (not part of the default run): the 7B M = 1 GEMV
+    (K=4096, N=14336, 58.7 MB of weights a call) rotated over 1 .. 12 weight
+    copies, and the SmolVLM sweep (237 MB a grouped launch) over 1 .. 4 copies.
+    Once a timed repetition touches more than the 256 MB Infinity Cache the
+    rate stops depending on the copy count: that plateau is the HBM rate."""
+    rows = []
+    K, N = 4096, 14336
+    d = workloads.llm7b(K, N, 1, seed=2)
+    q, s, _ = aql.aql_quantize_weight_int8(d["w"].to(dev), aql.AQL_WQ_SYM127)
+    x = d["x"].to(dev)
+    y = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
+    qs = [q] + [q.clone() for _ in range(11)]
+    nb = N * K + 4 * N + 2 * K + 2 * N
+    for c in (1, 2, 3, 4, 6, 8, 12):
+        fn = lambda i: aql.aql_linear_w8a16(x, qs[i % c], s, None, y)
+        med, _ = event_time_ms(torch, fn, 120, c)
+        row = {"workload": f"llm7b_w8a16 K={K} N={N} M=1, {c} copies", "working_set_MB": c * nb / 1e6,
+               "us": med * 1e3, "GB/s": nb / (med * 1e-3) / 1e9}
+        say(row)
+        rows.append(row)
+    del qs, q
+    torch.cuda.empty_cache()
+    layers = workloads.smolvlm(seed=0)
+    base, xs = [], []
+    for L in layers:
+        for wn, xn in (("w_up", "x_up"), ("w_gate", "x_up"), ("w_down", "x_down")):
+            qq, ss, _ = aql.aql_quantize_weight_int8(L[wn].to(dev), aql.AQL_WQ_SYM127)
+            xx = L[xn].to(dev)
+            base.append((xx, qq, ss, torch.empty(1, qq.shape[0], dtype=torch.bfloat16, device=dev)))
+    del layers
+    step = sum(qq.numel() + 4 * qq.shape[0] + 2 * xx.numel() + 2 * qq.shape[0]
+               for xx, qq, ss, _ in base)
+    sets = [base] + [[(xx, qq.clone(), ss, yy) for xx, qq, ss, yy in base] for _ in range(3)]
+    plans = [aql.aql_w8a16_group_plan([(xx, qq, ss, None, yy) for xx, qq, ss, yy in st])
+             for st in sets]
+    for c in (1, 2, 3, 4):
+        fn = lambda i: aql.aql_linear_w8a16_grouped(*plans[i % c])
+        med, _ = event_time_ms(torch, fn, 200, c)
+        row = {"workload": f"smolvlm500m_decode_sweep, {c} copies", "working_set_MB": c * step / 1e6,
+               "us": med * 1e3, "GB/s": step / (med * 1e-3) / 1e9}
+        say(row)
+        rows.append(row)
+    return rows
+
+
+def sec_oracle(torch, aql, workloads, dev):
+    """Oracle timing (not part of the default run): the CPU oracle at full size
+    on each workload, OpenMP over all host cores, median of 3 (one run where a
+    single run takes over 10 s); beside it the GPU time of the same call on one
+    weight buffer (so the weights may sit in the Infinity Cache: the bench rows
+    give the HBM rates)."""
+    import numpy as np
+
+    import oracle
+
+    def cpu_ms(fn, reps=3):
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append((time.perf_counter() - t0) * 1e3)
+            if ts[-1] > 10e3:
+                break
+        return statistics.median(ts)
+
+    def gpu_us(fn):
+        fn(0)
+        med, _ = event_time_ms(torch, fn, 20, 1, trials=3)
+        return med * 1e3
+
+    rows = []
+
+    def add(name, o_ms, g_us):
+        row = {"workload": name, "oracle_ms": o_ms, "gpu_us": g_us, "ratio": o_ms * 1e3 / g_us,
+               "cores": oracle.threads()}
+        say(row)
+        rows.append(row)
+
+    t = workloads.tiny()
+    wq, ws, _ = oracle.quantize_weight_int8(t["w"].numpy(), 0)
+    xb = workloads.bf16_bits(t["x"])
+    wdv = t["w"].to(dev)
+    qd, sd, _ = aql.aql_quantize_weight_int8(wdv, aql.AQL_WQ_SYM127)
+    xdv = t["x"].to(dev)
+    add("c1 tiny quantize + GEMV", cpu_ms(lambda: (oracle.quantize_weight_int8(t["w"].numpy(), 0),
+                                               oracle.linear_w8a16(xb, wq, ws))),
+        gpu_us(lambda i: (aql.aql_quantize_weight_int8(wdv, aql.AQL_WQ_SYM127, qd, sd),
+                          aql.aql_linear_w8a16(xdv, qd, sd))))
+    for K, N in workloads.LLM7B_SHAPES:
+        d = workloads.llm7b(K, N, 16, seed=2)
+        q, s, _ = oracle.quantize_weight_int8(d["w"].numpy(), 0)
+        qg, sg, _ = aql.aql_quantize_weight_int8(d["w"].to(dev), aql.AQL_WQ_SYM127)
+        for M in (1, 4, 16):
+            xm = d["x"][:M]
+            xbits = workloads.bf16_bits(xm)
+            xg = xm.to(dev)
+            add(f"c3 7B W8A16 K={K} N={N} M={M}", cpu_ms(lambda: oracle.linear_w8a16(xbits, q, s)),
+                gpu_us(lambda i: aql.aql_linear_w8a16(xg, qg, sg)))
+        del d, qg
+    tp = workloads.two_pass(seed=0)
+    xnp = tp["x"].numpy()
+    s1, z1, _ = oracle.choose_qparams_rows(np.ascontiguousarray(xnp[1:].reshape(1, -1)),
+                                           quantize=False)
+    s1, z1 = float(s1[0]), int(z1[0])
+    s2 = float(np.float32(s1) / np.float32(255.0))
+    q, ws8, wsum = oracle.quantize_weight_int8(tp["w"].numpy(), 1)
+    qg, wsg, wsumg = aql.aql_quantize_weight_int8(tp["w"].to(dev), aql.AQL_WQ_SYM127_5)
+    xg = tp["x"].to(dev)
+    add("c4 W8A8 two-pass M=512 K=N=4096",
+        cpu_ms(lambda: oracle.linear_q8ta_q8csw(xnp, s1, z1, q, ws8, two_pass=True, s2=s2, z2=0)),
+        gpu_us(lambda i: aql.aql_linear_q8ta_q8csw(xg, s1, z1, qg, wsumg, wsg, two_pass=True, s2=s2,
+                                                   z2=0)))
+    del tp, qg, xg
+    w = workloads.dyn8da4w(4, seed=1)["w"]
+    q4, gs, _ = oracle.quantize_weight_q4gsw(w.numpy())
+    q4g, gsg, gsumg = aql.aql_quantize_weight_q4gsw(w.to(dev))
+    del w
+    for M in (4, 128, 2048):
+        x = workloads.dyn8da4w(M, seed=2)["x"]
+        xn = x.numpy()
+        xg = x.to(dev)
+        add(f"c5 8da4w M={M} K=4096 N=11008",
+            cpu_ms(lambda: oracle.linear_dq8ca(xn, q4, gs, wfmt=oracle.W_Q4GSW, group=32)),
+            gpu_us(lambda i: aql.aql_linear_dq8ca(xg, q4g, gsg, gsumg, wfmt=aql.AQL_W_Q4GSW,
+                                                  group=32)))
+    return rows
+
+
 # ------------------------------------------------------------- CPU baseline
 
 
@@ -545,7 +675,8 @@ def main():
     secondary = []
     if args.only is not None and args.only != "sweep":
         fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant,
-              "calib": sec_calib, "copy": sec_copy, "gptq": sec_gptq}[args.only]
+              "calib": sec_calib, "copy": sec_copy, "gptq": sec_gptq, "wsweep": sec_wsweep,
+              "oracle": sec_oracle}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
         return
     calls, step_bytes, nbytes, layers = sweep_workload(torch, aql, workloads, dev)

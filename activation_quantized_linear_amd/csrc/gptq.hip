@@ -169,17 +169,21 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // earlier panels' updates. Every workgroup factors the diagonal block (lane t
 // holds row t); workgroup 0 stores it, workgroup g >= 1 then solves rows
 // k0 + 32 + 64 (g - 1) .. + 63 of the panel (lane t, row t). Both are
-// right-looking: at step k the new column k of L (lane j's value, read with
-// readlane) adds its term k to every later element's running sum, so each sum
-// still runs over k in ascending order. Past the matrix the diagonal block is
+// right-looking: at step k the new column k of L adds its term k to every
+// later element's running sum, so each sum still runs over k in ascending
+// order. The diagonal block's columns go through LDS, column-major (Lc[k][j] =
+// L[j][k]): the wave writes column k and reads it back (LDS serves one wave's
+// accesses in order); the row solve, whose columns are all known, reads
+// column k + 1 while step k computes. Past the matrix the diagonal block is
 // padded with an identity, which keeps the padded pivots at 1.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_chol_panel(
     const double *__restrict__ A, const double *__restrict__ acc, double *__restrict__ L,
     int64_t K, int64_t k0, int32_t *info, int32_t code0) {
-  __shared__ double Da[PB][PB + 1];  // diagonal block of A (row-major)
-  __shared__ double Dc[PB][PB + 1];  // ... of acc
-  __shared__ double R[64][PB + 1];   // this workgroup's rows of A
-  __shared__ double S[64][PB + 1];   // ... of acc
+  __shared__ double Da[PB][PB + 1];                          // diagonal block of A (row-major)
+  __shared__ double Dc[PB][PB + 1];                          // ... of acc
+  __shared__ __attribute__((aligned(16))) double Lc[PB][PB];  // ... of L, column-major
+  __shared__ double R[64][PB + 1];                           // this workgroup's rows of A
+  __shared__ double S[64][PB + 1];                           // ... of acc
   const int t = threadIdx.x, tr = t & (PB - 1);
   const int bn = (int)(K - k0 < PB ? K - k0 : PB);
   constexpr int DM = PB * PB / 64;  // diagonal-block elements a thread stages
@@ -224,53 +228,92 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   __syncthreads();
 
   // diagonal block: lane t (and t + 32, a copy) holds row tr; sd[j] is the
-  // running sum of element (tr, j)
-  double sd[PB], lr[PB];
+  // running sum of element (tr, j). Each step's updates are pinned to that
+  // step: left free, the compiler defers them to where the sums are next read
+  // and holds every column in registers meanwhile.
+  double sd[PB];
 #pragma unroll
   for (int j = 0; j < PB; ++j) sd[j] = Dc[tr][j];
+  int bad = 0;
 #pragma unroll
   for (int k = 0; k < PB; ++k) {
     const double d = readlane_f64(Da[tr][k], k) - readlane_f64(sd[k], k);
-    if (info && t == 0 && k < bn && !(d > 0.0)) atomicCAS(info, 0, code0 + k + 1);
+    const bool fail = (k < bn) & !(d > 0.0);
+    bad = ((bad == 0) & fail) ? code0 + k + 1 : bad;
     const double lkk = sqrt(d);
-    const double l = tr == k ? lkk : (Da[tr][k] - sd[k]) / lkk;
-    lr[k] = l;
+    const double below = (Da[tr][k] - sd[k]) / lkk;
+    const double l = tr == k ? lkk : below;
+    Lc[k][tr] = l;  // lanes t and t + 32 store the same value
+    double col[PB];
 #pragma unroll
-    for (int j = k + 1; j < PB; ++j) sd[j] = sd[j] + l * readlane_f64(l, j);
+    for (int p = (k + 1) / 2; p < PB / 2; ++p) {
+      const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[k][2 * p]);
+      col[2 * p] = v.x;
+      col[2 * p + 1] = v.y;
+    }
+#pragma unroll
+    for (int j = k + 1; j < PB; ++j) {
+      sd[j] = sd[j] + l * col[j];
+      asm volatile("" : "+v"(sd[j]));  // the update happens in this step
+    }
   }
+  if (info && bad && t == 0) atomicCAS(info, 0, bad);
   if (blockIdx.x == 0) {
     if (t < bn) {
 #pragma unroll
       for (int c = 0; c < PB; ++c)
-        if (c < bn) L[(k0 + t) * K + k0 + c] = c <= t ? lr[c] : 0.0;
+        if (c < bn) L[(k0 + t) * K + k0 + c] = c <= t ? Lc[c][t] : 0.0;
     }
     return;
   }
 
-  // rows below: lane t holds row r0 + t; lr[k] of lane j is L[k0 + j][k0 + k]
+  // rows below: lane t holds row r0 + t; column k of the block is Lc[k][.],
+  // read one step ahead. Each new value replaces the element of A it came
+  // from in R, and the rows go out whole at the end.
   double sr[PB];
 #pragma unroll
   for (int j = 0; j < PB; ++j) sr[j] = S[t][j];
-  const int64_t row = r0 + t;
+  double col[2][PB];
+#pragma unroll
+  for (int p = 0; p < PB / 2; ++p) {
+    const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[0][2 * p]);
+    col[0][2 * p] = v.x;
+    col[0][2 * p + 1] = v.y;
+  }
 #pragma unroll
   for (int k = 0; k < PB; ++k) {
-    const double l = (R[t][k] - sr[k]) / readlane_f64(lr[k], k);
-    if (row < K) L[row * K + k0 + k] = l;
+    if (k + 1 < PB) {
 #pragma unroll
-    for (int j = k + 1; j < PB; ++j) sr[j] = sr[j] + l * readlane_f64(lr[k], j);
+      for (int p = (k + 1) / 2; p < PB / 2; ++p) {
+        const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[k + 1][2 * p]);
+        col[(k + 1) & 1][2 * p] = v.x;
+        col[(k + 1) & 1][2 * p + 1] = v.y;
+      }
+    }
+    const double l = (R[t][k] - sr[k]) / col[k & 1][k];
+    R[t][k] = l;
+#pragma unroll
+    for (int j = k + 1; j < PB; ++j) {
+      sr[j] = sr[j] + l * col[k & 1][j];
+      asm volatile("" : "+v"(sr[j]));  // the update happens in this step
+    }
   }
+  __syncthreads();
+  for (int r = t / PB; r < 64; r += 64 / PB)
+    if (r0 + r < K && tr < bn) L[(r0 + r) * K + k0 + tr] = R[r][tr];
 }
 
 // Rows [k0, k0 + bn) of Xm = L^-1, one lane a column j < k0 + bn:
 // Xm[i][j] = 1 / L[i][i] (i == j), -(sum_{k=j}^{i-1} L[i][k] Xm[k][j]) / L[i][i]
 // (i > j), 0 (i < j). acc[i][j] holds the sum over k < k0 (the terms with k < j
 // are zero). Right-looking: Xm[k][j] adds its term to rows i > k at step k.
-// Lane r (and r + 32) holds row r of L's diagonal block, read with readlane.
-// Stored transposed: X[j][i] = Xm[i][j].
+// L's diagonal block sits in LDS column-major; column i + 1 is read while step
+// i computes. Stored transposed: X[j][i] = Xm[i][j].
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_trinv_panel(
     const double *__restrict__ L, const double *__restrict__ acc, double *__restrict__ X,
     int64_t K, int64_t k0) {
-  __shared__ double V[PB][65];  // [i][t]: Xm[k0 + i][j]
+  __shared__ __attribute__((aligned(16))) double Lc[PB][PB];  // Lc[i][r] = L[k0 + r][k0 + i]
+  __shared__ double V[PB][65];                                // [i][t]: Xm[k0 + i][j]
   const int t = threadIdx.x, tr = t & (PB - 1);
   const int bn = (int)(K - k0 < PB ? K - k0 : PB);
   const int64_t k1 = k0 + bn;
@@ -286,14 +329,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int c = 0; c < PB; ++c) ld[c] = tr < bn && c <= tr ? ld[c] : (c == tr ? 1.0 : 0.0);
 #pragma unroll
   for (int r = 0; r < PB; ++r) sv[r] = r < bn && j < k1 ? sv[r] : 0.0;
+  if (t < PB) {
+#pragma unroll
+    for (int c = 0; c < PB; ++c) Lc[c][tr] = ld[c];
+  }
+  __syncthreads();
+  double col[2][PB];
+#pragma unroll
+  for (int p = 0; p < PB / 2; ++p) {
+    const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[0][2 * p]);
+    col[0][2 * p] = v.x;
+    col[0][2 * p + 1] = v.y;
+  }
 #pragma unroll
   for (int i = 0; i < PB; ++i) {
+    if (i + 1 < PB) {
+#pragma unroll
+      for (int p = (i + 1) / 2; p < PB / 2; ++p) {
+        const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[i + 1][2 * p]);
+        col[(i + 1) & 1][2 * p] = v.x;
+        col[(i + 1) & 1][2 * p + 1] = v.y;
+      }
+    }
     const int64_t gi = k0 + i;
-    const double v = (gi == j ? 1.0 : -sv[i]) / readlane_f64(ld[i], i);
+    const double v = (gi == j ? 1.0 : -sv[i]) / col[i & 1][i];
     const double x = gi < j ? 0.0 : v;
     V[i][t] = x;
 #pragma unroll
-    for (int r = i + 1; r < PB; ++r) sv[r] = sv[r] + readlane_f64(ld[i], r) * x;
+    for (int r = i + 1; r < PB; ++r) sv[r] = sv[r] + col[i & 1][r] * x;
+    __builtin_amdgcn_sched_barrier(0);  // keep the column reads one step ahead, no further
   }
   __syncthreads();
   for (int r = t / PB; r < 64; r += 64 / PB)

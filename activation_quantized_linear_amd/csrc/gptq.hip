@@ -167,15 +167,15 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
 // One 32-column panel [k0, k0 + bn) of the lower Cholesky factor L of A, in
 // one wave. acc[i][j] holds sum_{k < k0} L[i][k] L[j][k] (ascending k) from the
 // earlier panels' updates. Every workgroup factors the diagonal block (lane t
-// holds row t); workgroup 0 stores it, workgroup g >= 1 then solves rows
-// k0 + 32 + 64 (g - 1) .. + 63 of the panel (lane t, row t). Both are
-// right-looking: at step k the new column k of L adds its term k to every
-// later element's running sum, so each sum still runs over k in ascending
-// order. The diagonal block's columns go through LDS, column-major (Lc[k][j] =
-// L[j][k]): the wave writes column k and reads it back (LDS serves one wave's
-// accesses in order); the row solve, whose columns are all known, reads
-// column k + 1 while step k computes. Past the matrix the diagonal block is
-// padded with an identity, which keeps the padded pivots at 1.
+// holds row t & 31); workgroup 0 stores it, workgroup g >= 1 also solves rows
+// k0 + 32 + 64 (g - 1) .. + 63 of the panel (lane t, row t) in the same steps:
+// step k needs only column k of the block, so the two solves' divisions
+// overlap. Both are right-looking: at step k the new column k of L adds its
+// term k to every later element's running sum, so each sum still runs over k
+// in ascending order. The block's column k goes through LDS, column-major
+// (Lc[k][j] = L[j][k]): the wave writes it and reads it back (LDS serves one
+// wave's accesses in order). Past the matrix the diagonal block is padded
+// with an identity, which keeps the padded pivots at 1.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_chol_panel(
     const double *__restrict__ A, const double *__restrict__ acc, double *__restrict__ L,
     int64_t K, int64_t k0, int32_t *info, int32_t code0) {
@@ -187,10 +187,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int t = threadIdx.x, tr = t & (PB - 1);
   const int bn = (int)(K - k0 < PB ? K - k0 : PB);
   constexpr int DM = PB * PB / 64;  // diagonal-block elements a thread stages
+  const bool rows = blockIdx.x > 0;
   const int64_t r0 = k0 + PB + (int64_t)(blockIdx.x - 1) * 64;
   {
-    // all loads first, then the selects (the unrolled code keeps source order)
-    double va[DM], vc[DM];
+    // all loads first, then the selects (the unrolled code keeps source order);
+    // workgroup 0 has no rows and reads element 0 in their place
+    double va[DM], vc[DM], ra[PB], rc[PB];
 #pragma unroll
     for (int m = 0; m < DM; ++m) {
       const int r = m * (64 / PB) + t / PB;
@@ -198,15 +200,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       va[m] = A[e];
       vc[m] = acc[e];
     }
-    double ra[PB], rc[PB];
-    if (blockIdx.x > 0) {
 #pragma unroll
-      for (int m = 0; m < PB; ++m) {
-        const int r = m * (64 / PB) + t / PB;
-        const int64_t e = r0 + r < K ? (r0 + r) * K + k0 + tr : 0;
-        ra[m] = A[e];
-        rc[m] = acc[e];
-      }
+    for (int m = 0; m < PB; ++m) {
+      const int r = m * (64 / PB) + t / PB;
+      const int64_t e = rows && r0 + r < K ? (r0 + r) * K + k0 + tr : 0;
+      ra[m] = A[e];
+      rc[m] = acc[e];
     }
 #pragma unroll
     for (int m = 0; m < DM; ++m) {
@@ -215,25 +214,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
       Da[r][tr] = ok ? va[m] : (r == tr ? 1.0 : 0.0);
       Dc[r][tr] = ok ? vc[m] : 0.0;
     }
-    if (blockIdx.x > 0) {
 #pragma unroll
-      for (int m = 0; m < PB; ++m) {
-        const int r = m * (64 / PB) + t / PB;
-        const bool ok = r0 + r < K;
-        R[r][tr] = ok ? ra[m] : 0.0;
-        S[r][tr] = ok ? rc[m] : 0.0;
-      }
+    for (int m = 0; m < PB; ++m) {
+      const int r = m * (64 / PB) + t / PB;
+      const bool ok = rows && r0 + r < K;
+      R[r][tr] = ok ? ra[m] : 0.0;
+      S[r][tr] = ok ? rc[m] : 0.0;
     }
   }
   __syncthreads();
 
-  // diagonal block: lane t (and t + 32, a copy) holds row tr; sd[j] is the
-  // running sum of element (tr, j). Each step's updates are pinned to that
-  // step: left free, the compiler defers them to where the sums are next read
-  // and holds every column in registers meanwhile.
-  double sd[PB];
+  // sd[j]: running sum of diagonal-block element (tr, j); sr[j]: of element
+  // (r0 + t, j). Each step's updates are pinned to that step: left free, the
+  // compiler defers them to where the sums are next read and holds every
+  // column in registers meanwhile.
+  double sd[PB], sr[PB];
 #pragma unroll
-  for (int j = 0; j < PB; ++j) sd[j] = Dc[tr][j];
+  for (int j = 0; j < PB; ++j) {
+    sd[j] = Dc[tr][j];
+    sr[j] = S[t][j];
+  }
   int bad = 0;
 #pragma unroll
   for (int k = 0; k < PB; ++k) {
@@ -242,8 +242,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     bad = ((bad == 0) & fail) ? code0 + k + 1 : bad;
     const double lkk = sqrt(d);
     const double below = (Da[tr][k] - sd[k]) / lkk;
+    const double lrow = (R[t][k] - sr[k]) / lkk;
     const double l = tr == k ? lkk : below;
     Lc[k][tr] = l;  // lanes t and t + 32 store the same value
+    R[t][k] = lrow;  // the new value replaces the element of A it came from
     double col[PB];
 #pragma unroll
     for (int p = (k + 1) / 2; p < PB / 2; ++p) {
@@ -254,49 +256,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int j = k + 1; j < PB; ++j) {
       sd[j] = sd[j] + l * col[j];
-      asm volatile("" : "+v"(sd[j]));  // the update happens in this step
+      sr[j] = sr[j] + lrow * col[j];
+      asm volatile("" : "+v"(sd[j]), "+v"(sr[j]));  // the updates happen in this step
     }
   }
   if (info && bad && t == 0) atomicCAS(info, 0, bad);
-  if (blockIdx.x == 0) {
+  if (!rows) {
     if (t < bn) {
 #pragma unroll
       for (int c = 0; c < PB; ++c)
         if (c < bn) L[(k0 + t) * K + k0 + c] = c <= t ? Lc[c][t] : 0.0;
     }
     return;
-  }
-
-  // rows below: lane t holds row r0 + t; column k of the block is Lc[k][.],
-  // read one step ahead. Each new value replaces the element of A it came
-  // from in R, and the rows go out whole at the end.
-  double sr[PB];
-#pragma unroll
-  for (int j = 0; j < PB; ++j) sr[j] = S[t][j];
-  double col[2][PB];
-#pragma unroll
-  for (int p = 0; p < PB / 2; ++p) {
-    const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[0][2 * p]);
-    col[0][2 * p] = v.x;
-    col[0][2 * p + 1] = v.y;
-  }
-#pragma unroll
-  for (int k = 0; k < PB; ++k) {
-    if (k + 1 < PB) {
-#pragma unroll
-      for (int p = (k + 1) / 2; p < PB / 2; ++p) {
-        const f64x2 v = *reinterpret_cast<const f64x2 *>(&Lc[k + 1][2 * p]);
-        col[(k + 1) & 1][2 * p] = v.x;
-        col[(k + 1) & 1][2 * p + 1] = v.y;
-      }
-    }
-    const double l = (R[t][k] - sr[k]) / col[k & 1][k];
-    R[t][k] = l;
-#pragma unroll
-    for (int j = k + 1; j < PB; ++j) {
-      sr[j] = sr[j] + l * col[k & 1][j];
-      asm volatile("" : "+v"(sr[j]));  // the update happens in this step
-    }
   }
   __syncthreads();
   for (int r = t / PB; r < 64; r += 64 / PB)

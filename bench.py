@@ -473,7 +473,8 @@ def sec_wsweep(torch, aql, workloads, dev):
 def sec_oracle(torch, aql, workloads, dev):
     """Oracle timing (not part of the default run): the CPU oracle at full size
     on each workload, OpenMP over all host cores, median of 3 (one run where a
-    single run takes over 10 s); beside it the GPU time of the same call on one
+    single run takes over 10 s), and one run on a single thread (skipped for
+    8da4w M=2048, about 90 s); beside it the GPU time of the same call on one
     weight buffer (so the weights may sit in the Infinity Cache: the bench rows
     give the HBM rates)."""
     import numpy as np
@@ -497,9 +498,18 @@ def sec_oracle(torch, aql, workloads, dev):
 
     rows = []
 
-    def add(name, o_ms, g_us):
+    def one_thread_ms(fn):
+        oracle.set_threads(1)
+        try:
+            return cpu_ms(fn, reps=1)
+        finally:
+            oracle.set_threads(None)
+
+    def add(name, fn, g_us, single=True):
+        o_ms = cpu_ms(fn)
         row = {"workload": name, "oracle_ms": o_ms, "gpu_us": g_us, "ratio": o_ms * 1e3 / g_us,
-               "cores": oracle.threads()}
+               "cores": oracle.threads(),
+               "oracle_ms_1_thread": one_thread_ms(fn) if single else None}
         say(row)
         rows.append(row)
 
@@ -509,8 +519,8 @@ def sec_oracle(torch, aql, workloads, dev):
     wdv = t["w"].to(dev)
     qd, sd, _ = aql.aql_quantize_weight_int8(wdv, aql.AQL_WQ_SYM127)
     xdv = t["x"].to(dev)
-    add("c1 tiny quantize + GEMV", cpu_ms(lambda: (oracle.quantize_weight_int8(t["w"].numpy(), 0),
-                                               oracle.linear_w8a16(xb, wq, ws))),
+    add("c1 tiny quantize + GEMV", lambda: (oracle.quantize_weight_int8(t["w"].numpy(), 0),
+                                            oracle.linear_w8a16(xb, wq, ws)),
         gpu_us(lambda i: (aql.aql_quantize_weight_int8(wdv, aql.AQL_WQ_SYM127, qd, sd),
                           aql.aql_linear_w8a16(xdv, qd, sd))))
     for K, N in workloads.LLM7B_SHAPES:
@@ -521,7 +531,7 @@ def sec_oracle(torch, aql, workloads, dev):
             xm = d["x"][:M]
             xbits = workloads.bf16_bits(xm)
             xg = xm.to(dev)
-            add(f"c3 7B W8A16 K={K} N={N} M={M}", cpu_ms(lambda: oracle.linear_w8a16(xbits, q, s)),
+            add(f"c3 7B W8A16 K={K} N={N} M={M}", lambda: oracle.linear_w8a16(xbits, q, s),
                 gpu_us(lambda i: aql.aql_linear_w8a16(xg, qg, sg)))
         del d, qg
     tp = workloads.two_pass(seed=0)
@@ -534,7 +544,7 @@ def sec_oracle(torch, aql, workloads, dev):
     qg, wsg, wsumg = aql.aql_quantize_weight_int8(tp["w"].to(dev), aql.AQL_WQ_SYM127_5)
     xg = tp["x"].to(dev)
     add("c4 W8A8 two-pass M=512 K=N=4096",
-        cpu_ms(lambda: oracle.linear_q8ta_q8csw(xnp, s1, z1, q, ws8, two_pass=True, s2=s2, z2=0)),
+        lambda: oracle.linear_q8ta_q8csw(xnp, s1, z1, q, ws8, two_pass=True, s2=s2, z2=0),
         gpu_us(lambda i: aql.aql_linear_q8ta_q8csw(xg, s1, z1, qg, wsumg, wsg, two_pass=True, s2=s2,
                                                    z2=0)))
     del tp, qg, xg
@@ -547,9 +557,10 @@ def sec_oracle(torch, aql, workloads, dev):
         xn = x.numpy()
         xg = x.to(dev)
         add(f"c5 8da4w M={M} K=4096 N=11008",
-            cpu_ms(lambda: oracle.linear_dq8ca(xn, q4, gs, wfmt=oracle.W_Q4GSW, group=32)),
+            lambda: oracle.linear_dq8ca(xn, q4, gs, wfmt=oracle.W_Q4GSW, group=32),
             gpu_us(lambda i: aql.aql_linear_dq8ca(xg, q4g, gsg, gsumg, wfmt=aql.AQL_W_Q4GSW,
-                                                  group=32)))
+                                                  group=32)),
+            single=M < 2048)
     return rows
 
 

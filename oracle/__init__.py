@@ -48,6 +48,7 @@ _SIGS = {
     "orc_gptq_hinv": [_p, _i64, _p],
     "orc_gptq_quantize": [_p, _i64, _i64, _p, _p, _p, _i64, _p, _i64, _p, _p],
     "orc_minmax_qparams": [_p, _p, _p],
+    "orc_set_threads": [_int],
 }
 
 
@@ -74,6 +75,12 @@ def _c(a, dtype):
     if a.dtype != dtype:
         raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
     return a
+
+
+def _shape(a, shape, what):
+    """Raise unless array a has exactly this shape (the C side trusts the sizes)."""
+    if a is not None and tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(a.shape)}")
 
 
 def _check(rc, name):
@@ -150,6 +157,7 @@ def gemm_i8(a, b):
     b = _c(b, np.int8)
     M, K = a.shape
     N = b.shape[0]
+    _shape(b, (N, K), "b")
     c = np.empty((M, N), np.int64)
     _check(lib().orc_gemm_i8_i64(_ptr(a), _ptr(b), M, N, K, _ptr(c)), "gemm_i8_i64")
     return c
@@ -164,6 +172,9 @@ def linear_w8a16(x_bf16, q, scale, bias_bf16=None):
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     M, K = x.shape
     N = q.shape[0]
+    _shape(q, (N, K), "q")
+    _shape(scale, (N,), "scale")
+    _shape(b, (N,), "bias")
     y = np.empty((M, N), np.float64)
     tol = np.empty((M, N), np.float64)
     _check(lib().orc_linear_w8a16(_ptr(x), M, K, _ptr(q), _ptr(scale), _ptr(b), N, _ptr(y),
@@ -178,6 +189,9 @@ def linear_w8a16_dequant_first(x_bf16, q, scale, bias_bf16=None):
     b = None if bias_bf16 is None else _c(bias_bf16, np.uint16)
     M, K = x.shape
     N = q.shape[0]
+    _shape(q, (N, K), "q")
+    _shape(scale, (N,), "scale")
+    _shape(b, (N,), "bias")
     y = np.empty((M, N), np.float64)
     _check(lib().orc_linear_w8a16_dequant_first(_ptr(x), M, K, _ptr(q), _ptr(scale), _ptr(b),
                                                 N, _ptr(y)), "linear_w8a16_dequant_first")
@@ -193,6 +207,9 @@ def linear_q8ta_q8csw(x, s1, z1, q, wscale, bias=None, two_pass=False, s2=None, 
     b = None if bias is None else _c(bias, np.float32)
     M, K = x.shape
     N = q.shape[0]
+    _shape(q, (N, K), "q")
+    _shape(wscale, (N,), "wscale")
+    _shape(b, (N,), "bias")
     out = {
         "y": np.empty((M, N), np.float64),
         "tol": np.empty((M, N), np.float64),
@@ -218,12 +235,28 @@ def linear_q8ta_dequant_first(xq1, xq2, s1, z1, q, wscale, bias=None, two_pass=F
     b = None if bias is None else _c(bias, np.float32)
     M, K = xq1.shape
     N = q.shape[0]
+    _shape(xq2, (M, K), "xq2")
+    _shape(q, (N, K), "q")
+    _shape(wscale, (N,), "wscale")
+    _shape(b, (N,), "bias")
     y = np.empty((M, N), np.float64)
     _check(lib().orc_linear_q8ta_dequant_first(
         _ptr(xq1), _ptr(xq2), M, K, np.float32(s1), int(z1), int(bool(two_pass)),
         np.float32(s2 if two_pass else 1.0), int(z2), _ptr(q), _ptr(wscale), _ptr(b), N,
         _ptr(y)), "linear_q8ta_dequant_first")
     return y
+
+
+def _wq_shapes(wq, wscale, b, N, K, wfmt, group):
+    if wfmt == W_Q8CSW:
+        _shape(wq, (N, K), "wq")
+        _shape(wscale, (N,), "wscale")
+    else:
+        if group <= 0 or K % group or group % 2:
+            raise ValueError("K must be a multiple of an even group")
+        _shape(wq, (N, K // 2), "wq")
+        _shape(wscale, (N, K // group), "wscale")
+    _shape(b, (N,), "bias")
 
 
 def linear_dq8ca(x, wq, wscale, wfmt=W_Q8CSW, group=0, bias=None):
@@ -238,6 +271,7 @@ def linear_dq8ca(x, wq, wscale, wfmt=W_Q8CSW, group=0, bias=None):
     N = wq.shape[0]
     wscale = _c(wscale, np.float32)
     b = None if bias is None else _c(bias, np.float32)
+    _wq_shapes(wq, wscale, b, N, K, wfmt, group)
     out = {
         "y": np.empty((M, N), np.float64),
         "tol": np.empty((M, N), np.float64),
@@ -261,6 +295,10 @@ def linear_dq8ca_dequant_first(xq, xs, xz, wq, wscale, K, wfmt=W_Q8CSW, group=0,
     N = wq.shape[0]
     wscale = _c(wscale, np.float32)
     b = None if bias is None else _c(bias, np.float32)
+    _shape(xq, (M, K), "xq")
+    _shape(xs, (M,), "xs")
+    _shape(xz, (M,), "xz")
+    _wq_shapes(wq, wscale, b, N, K, wfmt, group)
     y = np.empty((M, N), np.float64)
     _check(lib().orc_linear_dq8ca_dequant_first(_ptr(xq), _ptr(xs), _ptr(xz), M, K, int(wfmt),
                                                 _ptr(wq), _ptr(wscale), int(group), _ptr(b), N,
@@ -324,6 +362,7 @@ def gptq_damped(H, damp=0.01):
     """(damped Hessian float64 [K, K], dead columns bool [K]) of gptq_int8."""
     H = _c(H, np.float64)
     K = H.shape[0]
+    _shape(H, (K, K), "H")
     Hd = np.empty_like(H)
     dead = np.empty(K, np.uint8)
     _check(lib().orc_gptq_damp(_ptr(H), K, damp, _ptr(Hd), _ptr(dead)), "gptq_damp")
@@ -334,6 +373,7 @@ def gptq_hinv(Hd):
     """Upper factor hinv of Hd^-1 (hinv^T hinv = Hd^-1), float64 [K, K]."""
     Hd = _c(Hd, np.float64)
     K = Hd.shape[0]
+    _shape(Hd, (K, K), "Hd")
     hinv = np.empty_like(Hd)
     _check(lib().orc_gptq_hinv(_ptr(Hd), K, _ptr(hinv)), "gptq_hinv")
     return hinv
@@ -346,13 +386,17 @@ def gptq_int8(w, H, damp=0.01, block=128, rows=None, hinv=None):
     of the same damped Hessian."""
     w = _c(w, np.float32)
     N, K = w.shape
+    _shape(np.asarray(H), (K, K), "H")
     _, scale, _ = quantize_weight_int8(w, WQ_SYM127_5)
     Hd, dead = gptq_damped(H, damp)
     if hinv is None:
         hinv = gptq_hinv(Hd)
     hinv = _c(hinv, np.float64)
+    _shape(hinv, (K, K), "hinv")
     dead8 = dead.astype(np.uint8)
     rl = None if rows is None else np.ascontiguousarray(np.asarray(rows, np.int64))
+    if rl is not None and rl.size and (rl.min() < 0 or rl.max() >= N):
+        raise ValueError("rows out of range")
     R = N if rl is None else rl.size
     q = np.empty((R, K), np.int8)
     wsum = np.empty(R, np.int32)
@@ -362,7 +406,21 @@ def gptq_int8(w, H, damp=0.01, block=128, rows=None, hinv=None):
     return q, scale, wsum
 
 
-def threads():
-    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
+_THREADS = None
+
+
+def set_threads(n):
+    """Run the oracle's OpenMP loops on n threads (None: back to the default)."""
+    global _THREADS
+    _check(lib().orc_set_threads(int(n) if n else _default_threads()), "set_threads")
+    _THREADS = int(n) if n else None
+
+
+def _default_threads():
     v = os.environ.get("OMP_NUM_THREADS")
     return int(v) if v else os.cpu_count()
+
+
+def threads():
+    """OpenMP threads the oracle uses (set_threads, else OMP_NUM_THREADS, else all cores)."""
+    return _THREADS or _default_threads()

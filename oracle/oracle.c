@@ -32,6 +32,7 @@
  *                        choose_qparams_affine (8da4w)", the Impl paragraph
  */
 #include <math.h>
+#include <omp.h>
 #include <float.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -757,4 +758,12 @@ int orc_gptq_quantize(const float *w, int64_t N, int64_t K, const uint8_t *dead,
         free(err);
     }
     return bad ? ORC_BAD : ORC_OK;
+}
+
+/* Threads of the OpenMP loops above (n >= 1); the results do not depend on it. */
+int orc_set_threads(int n)
+{
+    if (n < 1) return ORC_BAD;
+    omp_set_num_threads(n);
+    return ORC_OK;
 }

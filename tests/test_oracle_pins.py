@@ -638,3 +638,66 @@ def test_gptq_lowers_the_hessian_weighted_error():
     # the block size changes only the rounding of the updates
     q2, _, _ = oracle.gptq_int8(w, H, block=128)
     assert (q2 != q).mean() < 0.002
+
+
+# ------------------------------------------------------------- thread count
+
+
+def test_oracle_results_do_not_depend_on_the_thread_count():
+    """The OpenMP loops split only independent output rows, so one thread and
+    all threads give the same bits (quantizer, GEMV, W8A8 two-pass, 8da4w)."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((37, 96)) * 0.02).astype(np.float32)
+    x = rng.standard_normal((5, 96)).astype(np.float32)
+    xb = workloads.bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+
+    def run():
+        q, s, wsum = oracle.quantize_weight_int8(w, oracle.WQ_SYM127_5)
+        y16 = oracle.linear_w8a16(xb, q, s)
+        y8 = oracle.linear_q8ta_q8csw(x, 0.03, 3, q, s, two_pass=True, s2=0.03 / 255, z2=0)
+        q4, gs, _ = oracle.quantize_weight_q4gsw(w)
+        yd = oracle.linear_dq8ca(x, q4, gs, wfmt=oracle.W_Q4GSW, group=32)
+        return [q, s, wsum, y16, y8, q4, gs, yd]
+
+    many = run()
+    oracle.set_threads(1)
+    try:
+        assert oracle.threads() == 1
+        one = run()
+    finally:
+        oracle.set_threads(None)
+    def flat(items):
+        out = []
+        for v in items:
+            if isinstance(v, dict):
+                out += [v[k] for k in sorted(v) if v[k] is not None]
+            elif isinstance(v, tuple):
+                out += list(v)
+            else:
+                out.append(v)
+        return out
+
+    a, b = flat(many), flat(one)
+    assert len(a) == len(b) > 8
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_oracle_rejects_mismatched_shapes():
+    """The C side trusts the sizes it is given, so the wrappers refuse operands
+    whose shapes disagree instead of reading past them."""
+    q = np.zeros((4, 32), np.int8)
+    s = np.ones(4, np.float32)
+    with pytest.raises(ValueError):
+        oracle.linear_w8a16(np.zeros((2, 64), np.uint16), q, s)
+    with pytest.raises(ValueError):
+        oracle.linear_w8a16(np.zeros((2, 32), np.uint16), q, np.ones(3, np.float32))
+    with pytest.raises(ValueError):
+        oracle.linear_q8ta_q8csw(np.zeros((2, 16), np.float32), 1.0, 0, q, s)
+    with pytest.raises(ValueError):
+        oracle.linear_dq8ca(np.zeros((2, 32), np.float32), np.zeros((4, 8), np.uint8),
+                            np.ones((4, 1), np.float32), wfmt=oracle.W_Q4GSW, group=32)
+    with pytest.raises(ValueError):
+        oracle.gemm_i8(np.zeros((2, 31), np.int8), q)
+    with pytest.raises(ValueError):
+        oracle.gptq_int8(np.zeros((4, 8), np.float32), np.eye(9))

@@ -505,10 +505,11 @@ def sec_oracle(torch, aql, workloads, dev):
         finally:
             oracle.set_threads(None)
 
-    def add(name, fn, g_us, single=True):
+    def add(name, fn, g_us, rows_x, single=True):
+        # rows_x: rows of x, over which the oracle's linears split their threads
         o_ms = cpu_ms(fn)
         row = {"workload": name, "oracle_ms": o_ms, "gpu_us": g_us, "ratio": o_ms * 1e3 / g_us,
-               "cores": oracle.threads(),
+               "cores": oracle.threads(), "threads_working": min(oracle.threads(), rows_x),
                "oracle_ms_1_thread": one_thread_ms(fn) if single else None}
         say(row)
         rows.append(row)
@@ -522,7 +523,7 @@ def sec_oracle(torch, aql, workloads, dev):
     add("c1 tiny quantize + GEMV", lambda: (oracle.quantize_weight_int8(t["w"].numpy(), 0),
                                             oracle.linear_w8a16(xb, wq, ws)),
         gpu_us(lambda i: (aql.aql_quantize_weight_int8(wdv, aql.AQL_WQ_SYM127, qd, sd),
-                          aql.aql_linear_w8a16(xdv, qd, sd))))
+                          aql.aql_linear_w8a16(xdv, qd, sd))), 1)
     for K, N in workloads.LLM7B_SHAPES:
         d = workloads.llm7b(K, N, 16, seed=2)
         q, s, _ = oracle.quantize_weight_int8(d["w"].numpy(), 0)
@@ -532,7 +533,7 @@ def sec_oracle(torch, aql, workloads, dev):
             xbits = workloads.bf16_bits(xm)
             xg = xm.to(dev)
             add(f"c3 7B W8A16 K={K} N={N} M={M}", lambda: oracle.linear_w8a16(xbits, q, s),
-                gpu_us(lambda i: aql.aql_linear_w8a16(xg, qg, sg)))
+                gpu_us(lambda i: aql.aql_linear_w8a16(xg, qg, sg)), M)
         del d, qg
     tp = workloads.two_pass(seed=0)
     xnp = tp["x"].numpy()
@@ -546,7 +547,7 @@ def sec_oracle(torch, aql, workloads, dev):
     add("c4 W8A8 two-pass M=512 K=N=4096",
         lambda: oracle.linear_q8ta_q8csw(xnp, s1, z1, q, ws8, two_pass=True, s2=s2, z2=0),
         gpu_us(lambda i: aql.aql_linear_q8ta_q8csw(xg, s1, z1, qg, wsumg, wsg, two_pass=True, s2=s2,
-                                                   z2=0)))
+                                                   z2=0)), 512)
     del tp, qg, xg
     w = workloads.dyn8da4w(4, seed=1)["w"]
     q4, gs, _ = oracle.quantize_weight_q4gsw(w.numpy())
@@ -560,7 +561,7 @@ def sec_oracle(torch, aql, workloads, dev):
             lambda: oracle.linear_dq8ca(xn, q4, gs, wfmt=oracle.W_Q4GSW, group=32),
             gpu_us(lambda i: aql.aql_linear_dq8ca(xg, q4g, gsg, gsumg, wfmt=aql.AQL_W_Q4GSW,
                                                   group=32)),
-            single=M < 2048)
+            M, single=M < 2048)
     return rows
 
 
@@ -591,9 +592,13 @@ def cpu_baseline(layers, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": done_b / el / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+    # the oracle's OpenMP loops split output rows of x, and a decode GEMV has one
+    rows_x = max(x.shape[0] for x, _, _ in prepared)
+    return {"value": done_b / el / 1e9, "unit": "GB/s", "cores": min(oracle.threads(), rows_x),
+            "kind": "oracle",
             "sample": f"{gemvs} of the decode sweep's W8A16 GEMVs (in sweep order, fp64 sums), "
-                      f"{el:.1f} s on the host"}
+                      f"{el:.1f} s on the host; the oracle splits rows of x over threads, so "
+                      f"{min(oracle.threads(), rows_x)} of {oracle.threads()} work"}
 
 
 def sec_copy(torch, aql, workloads, dev, mib=256, reps=20):

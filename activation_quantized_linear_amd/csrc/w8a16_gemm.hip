@@ -233,6 +233,206 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
   }
 }
 
+// Wide tile: 128 rows of x x 256 output channels, 8 waves side by side along
+// N, each 128 x 32 (8 x 2 MFMA tiles) over the whole 64-k stage (32 MFMAs a
+// stage, no K halves to add). The weights are the cheap operand (1 byte an
+// element against x's 2), so doubling the channels per tile cuts the operand
+// bytes per MFMA by a third: 32 KB a stage for 2 x 128 x 256 x 64 flops
+// instead of 24 KB for half that. Each wave widens only its own 32 channels
+// and uses every widened fragment for 8 MFMAs; with 2 x 4 waves of 64 x 64 the
+// widening was done twice and took ~20% longer.
+struct WideLds {
+  static constexpr int BM = 128, BNW = 256;
+  static constexpr int XS = BM * 128;           // x stage: 128 rows x 64 bf16
+  static constexpr int WS = BNW * 64;           // weight stage: 256 rows x 64 int8
+  static constexpr int STAGE = XS + WS;         // 32 KB
+  static constexpr int RING = STAGES * STAGE;   // 128 KB
+  static constexpr int TLD = BNW + 8;           // bf16 per staged output row
+  static constexpr int TILE = BM * TLD * 2;
+  static constexpr int BYTES = RING > TILE ? RING : TILE;
+};
+
+__global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restrict__ x,
+                                                         const int8_t *__restrict__ q,
+                                                         const float *__restrict__ scale,
+                                                         const uint16_t *__restrict__ bias,
+                                                         uint16_t *__restrict__ y, int64_t M,
+                                                         int64_t N, int64_t K, int tiles_m,
+                                                         int tiles_n) {
+  using L = WideLds;
+  constexpr int BM = L::BM, BNW = L::BNW, NL = 4;  // loads per wave per stage
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  const int nt = tiles_m * tiles_n;
+  const int lin = blockIdx.x;
+  int tile = lin;
+  if ((nt & 7) == 0) tile = (lin & 7) * (nt >> 3) + (lin >> 3);
+  const int tn = tile / tiles_m, tm = tile % tiles_m;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNW;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave;  // 32 channels a wave
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t mval = M - m0 < BM ? M - m0 : BM;
+  const int64_t nval = N - n0 < BNW ? N - n0 : BNW;
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, (uint32_t)(mval * K * 2));
+  const __amdgpu_buffer_rsrc_t rq = rsrc(q + n0 * K, (uint32_t)(nval * K));
+
+  // Loads per stage: 16 x-slots (8 rows x 128 B) and 16 weight slots (16 rows
+  // x 64 B); load qq of wave w is x-slot 8 qq + w (qq < 2), else weight slot
+  // 8 (qq - 2) + w.
+  uint32_t off[NL], ldso[NL], kstep[NL];
+  int kin_lim[NL];
+#pragma unroll
+  for (int qq = 0; qq < NL; ++qq) {
+    if (qq < 2) {
+      const int slot = qq * 8 + wave;
+      const int row = 8 * slot + (lane >> 3), c = (lane & 7) ^ swz_x(row);
+      off[qq] = (uint32_t)row * (uint32_t)(2 * K) + 16u * c;
+      ldso[qq] = (uint32_t)(slot * 1024);
+      kstep[qq] = 128;
+      kin_lim[qq] = (int)((2 * K - 16 * c + 127) / 128);
+    } else {
+      const int slot = (qq - 2) * 8 + wave;
+      const int row = 16 * slot + (lane >> 2), c = (lane & 3) ^ swz_w(row);
+      off[qq] = (uint32_t)row * (uint32_t)K + 16u * c;
+      ldso[qq] = (uint32_t)(L::XS + slot * 1024);
+      kstep[qq] = 64;
+      kin_lim[qq] = (int)((K - 16 * c + 63) / 64);
+    }
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int qq = 0; qq < NL; ++qq) {
+      const uint32_t dst = lds_base + (uint32_t)((kt % STAGES) * L::STAGE) + ldso[qq];
+      const int o = kt < kin_lim[qq] ? (int)(off[qq] + kstep[qq] * (uint32_t)kt) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qq < 2 ? rx : rq, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16, o, 0,
+          0, 0);
+    }
+  };
+
+  // fragment offsets within a stage, per 32-k half kk of the stage
+  int fxo[2][8], fwo[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int R = i * 16 + r;
+      fxo[kk][i] = R * 128 + 16 * ((4 * kk + g) ^ swz_x(R));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int S = wn * 32 + j * 16 + r;
+      fwo[kk][j] = L::XS + S * 64 + 16 * ((2 * kk + (g >> 1)) ^ swz_w(S)) + 8 * (g & 1);
+    }
+  }
+
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int kt) {
+    const char *st = smem + (kt % STAGES) * L::STAGE;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 fa[8], fb[2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8 *>(st + fxo[kk][i]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const i32x2 w = *reinterpret_cast<const i32x2 *>(st + fwo[kk][j]);
+        fb[j] = widen8((uint32_t)w[0], (uint32_t)w[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (int)((K + BK - 1) / BK);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  int kt = 0;
+  for (; kt < nk - (STAGES - 1); ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
+    __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; slot of kt-1 free
+    issue(kt + STAGES - 1);
+    compute(kt);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this stage's fragment reads done
+  }
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t) {
+    if (kt < nk) {
+      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
+      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 3)));
+      else __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_barrier();
+      compute(kt);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+    ++kt;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+
+  // scale + bias + bf16 into the LDS output tile; acc[i][j] lane holds
+  // D[4g + v][r] of MFMA tile (i, j): row m, column n.
+  uint16_t *tl = reinterpret_cast<uint16_t *>(smem);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = wn * 32 + j * 16 + r;
+    const int64_t n = n0 + col;
+    const float s = n < N ? scale[n] : 0.0f;
+    const float b = (n < N && bias) ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        tl[(i * 16 + 4 * g + v) * L::TLD + col] = f32_to_bf16_rne(s * acc[i][j][v] + b);
+  }
+  __syncthreads();
+  // 32 lanes x 16 B per 512-byte row
+  const bool vec = (N & 7) == 0;
+  for (int u = tid; u < BM * 32; u += 512) {
+    const int row = u >> 5, c = u & 31;
+    const int64_t m = m0 + row, n = n0 + 8 * c;
+    if (m >= M || n >= N) continue;
+    const i32x4 val = *reinterpret_cast<const i32x4 *>(tl + row * L::TLD + 8 * c);
+    uint16_t *dst = y + m * N + n;
+    if (vec) {
+      *reinterpret_cast<i32x4 *>(dst) = val;
+    } else {
+      const uint16_t *h = reinterpret_cast<const uint16_t *>(&val);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) dst[e] = h[e];
+    }
+  }
+}
+
+hipError_t launch_wide(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
+                       const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
+  using L = WideLds;
+  static bool attr_set = false;
+  if (!attr_set) {  // more than 64 KB of dynamic LDS; a launch the limit refuses reports itself
+    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int tiles_m = (int)((M + L::BM - 1) / L::BM), tiles_n = (int)((N + L::BNW - 1) / L::BNW);
+  hipLaunchKernelGGL(k_w8a16_gemm_wide, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), L::BYTES,
+                     st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <int WM>
 hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
                      const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
@@ -252,10 +452,13 @@ hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, c
 
 }  // namespace
 
-// 128-row tiles when they alone fill the CUs, else 64-row tiles.
+// 128 x 256 tiles when they alone fill the CUs, else 128 x 128 tiles when
+// those do, else 64 x 128 tiles.
 hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                              hipStream_t st) {
+  const int64_t twide = ((M + WideLds::BM - 1) / WideLds::BM) * ((N + WideLds::BNW - 1) / WideLds::BNW);
+  if (twide >= 256) return launch_wide(x, M, K, q, scale, bias, N, y, st);
   const int64_t t128 = ((M + 127) / 128) * ((N + BN - 1) / BN);
   if (t128 >= 256) return launch_wm<2>(x, M, K, q, scale, bias, N, y, st);
   return launch_wm<1>(x, M, K, q, scale, bias, N, y, st);

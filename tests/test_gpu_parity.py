@@ -279,11 +279,13 @@ def test_w8a16_smolvlm_sweep():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 128, 64), (65, 129, 80), (128, 300, 1040), (200, 257, 4096),
-                                   (513, 130, 272), (1024, 2048, 512)])
+                                   (513, 130, 272), (1024, 2048, 512), (2000, 4100, 272),
+                                   (1920, 8200, 80)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_prefill_shapes(M, N, K, with_bias):
-    """Prefill-sized M runs the tiled bf16-MFMA GEMM (64- or 128-row tiles):
-    ragged M, N and K (K % 64 != 0), with and without bias."""
+    """Prefill-sized M runs the tiled bf16-MFMA GEMM (64 x 128, 128 x 128 or,
+    from 256 tiles on, 128 x 256 tiles): ragged M, N and K (K % 64 != 0), N
+    not a multiple of 8, with and without bias."""
     say("w8a16 prefill", M, N, K, with_bias)
     g = workloads.gen(700 + M + N + K)
     w = workloads.small_matrix(g, N, K, std=0.02)
@@ -295,10 +297,11 @@ def test_w8a16_prefill_shapes(M, N, K, with_bias):
 
 
 @pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
-def test_w8a16_llm7b_prefill_full_size(K, N):
-    """7B shapes at M = 512 (the tiled GEMM at its real size), checked on
-    sampled rows: the first and last rows and 6 random ones."""
-    M = 512
+@pytest.mark.parametrize("M", [512, 2048])
+def test_w8a16_llm7b_prefill_full_size(K, N, M):
+    """7B shapes at M = 512 and 2048 (the tiled GEMM at its real sizes, both
+    tile shapes), checked on sampled rows: the first and last rows and 6
+    random ones."""
     say("w8a16 7b prefill", K, N, M)
     d = workloads.llm7b(K, N, M, seed=6)
     q, s, _ = aql.aql_quantize_weight_int8(dev(d["w"]), aql.AQL_WQ_SYM127)

@@ -148,11 +148,15 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
       fa[i] = *reinterpret_cast<const i32x4 *>(st + fao[i]);
       fb[i] = *reinterpret_cast<const i32x4 *>(st + fbo[i]);
     }
+    // the MFMA run issues at raised wave priority, so the other wave of the
+    // SIMD fills the gaps with its loads instead of competing
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Prologue issues stages 0 .. STAGES-2 (ranges past K load zeros). The main
@@ -163,13 +167,20 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   int kt = 0;
-  for (; kt < nk - (STAGES - 1); ++kt) {
+  auto step = [&](int k) {
     wait_vm<4 * (STAGES - 2)>();
-    __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; slot of kt-1 free
-    issue(kt + STAGES - 1);
-    compute(kt);
+    __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
+    issue(k + STAGES - 1);
+    compute(k);
     wait_lgkm0();  // this stage's fragment reads done before its slot is refilled
+  };
+  // whole turns of the ring first: each stage's LDS offsets become constants
+  const int nmain = nk - (STAGES - 1);
+  for (; kt + STAGES - 1 < nmain; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) step(kt + u);
   }
+  for (; kt < nmain; ++kt) step(kt);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {

@@ -153,24 +153,33 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
       const i32x2 w = *reinterpret_cast<const i32x2 *>(st + fwo[i]);
       fb[i] = widen8((uint32_t)w[0], (uint32_t)w[1]);
     }
+    __builtin_amdgcn_s_setprio(1);  // as in the wide tile below
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   const int nk = (int)((K + BK - 1) / BK);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   int kt = 0;
-  for (; kt < nk - (STAGES - 1); ++kt) {
+  auto step = [&](int k) {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-    __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; slot of kt-1 free
-    issue(kt + STAGES - 1);
-    compute(kt);
+    __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
+    issue(k + STAGES - 1);
+    compute(k);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this stage's fragment reads done
+  };
+  // whole turns of the ring first: each stage's LDS offsets become constants
+  const int nmain = nk - (STAGES - 1);
+  for (; kt + STAGES - 1 < nmain; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) step(kt + u);
   }
+  for (; kt < nmain; ++kt) step(kt);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {
@@ -348,11 +357,15 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
         const i32x2 w = *reinterpret_cast<const i32x2 *>(st + fwo[kk][j]);
         fb[j] = widen8((uint32_t)w[0], (uint32_t)w[1]);
       }
+      // the MFMA run issues at raised wave priority, so the other wave of the
+      // SIMD fills the gaps with its loads and widening instead of competing
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
@@ -360,13 +373,20 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   int kt = 0;
-  for (; kt < nk - (STAGES - 1); ++kt) {
+  auto step = [&](int k) {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-    __builtin_amdgcn_s_barrier();  // stage kt complete everywhere; slot of kt-1 free
-    issue(kt + STAGES - 1);
-    compute(kt);
+    __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
+    issue(k + STAGES - 1);
+    compute(k);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this stage's fragment reads done
+  };
+  // whole turns of the ring first: each stage's LDS offsets become constants
+  const int nmain = nk - (STAGES - 1);
+  for (; kt + STAGES - 1 < nmain; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) step(kt + u);
   }
+  for (; kt < nmain; ++kt) step(kt);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {
@@ -452,13 +472,14 @@ hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, c
 
 }  // namespace
 
-// 128 x 256 tiles when they alone fill the CUs, else 128 x 128 tiles when
-// those do, else 64 x 128 tiles.
+// 128 x 256 tiles from 160 of them on (fewer than one per CU still beats the
+// smaller tiles' extra round), else 128 x 128 tiles when those fill the CUs,
+// else 64 x 128 tiles.
 hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                              hipStream_t st) {
   const int64_t twide = ((M + WideLds::BM - 1) / WideLds::BM) * ((N + WideLds::BNW - 1) / WideLds::BNW);
-  if (twide >= 256) return launch_wide(x, M, K, q, scale, bias, N, y, st);
+  if (twide >= 160) return launch_wide(x, M, K, q, scale, bias, N, y, st);
   const int64_t t128 = ((M + 127) / 128) * ((N + BN - 1) / BN);
   if (t128 >= 256) return launch_wm<2>(x, M, K, q, scale, bias, N, y, st);
   return launch_wm<1>(x, M, K, q, scale, bias, N, y, st);

@@ -25,7 +25,10 @@ as its host overhead exceeds its GPU time).
 Before the first timing, each run drives its workload back to back for ~50 ms
 of GPU time (settle()): coming out of idle the GPU streams memory about 10%
 slower for the first 10-20 ms of sustained load, and the figures here are
-steady-state ones.
+steady-state ones. Matrix-core rows (prefill GEMMs, W8A8, GPTQ) also run their
+own call for ~40 ms right before they are timed: their clock ramps again under
+their own load (an M = 2048 prefill call falls from ~285 to ~235 us over its
+first ~30 ms).
 
 cpu_baseline: the CPU oracle (test infrastructure; its only use here) timed on
 the host on a bounded sample of the headline workload.
@@ -82,17 +85,21 @@ def say(*a):
 _SETTLED = [False]
 
 
-def event_time_ms(torch, fn, reps, rotate, trials=5, graph=False):
+def event_time_ms(torch, fn, reps, rotate, trials=5, graph=False, warm_ms=0.0):
     """Per-call time (ms): HIP events on the current stream bracket `reps`
     back-to-back calls (rotating over `rotate` buffer sets); median of `trials`.
     Where the host keeps ahead of the GPU this is the GPU's time per call. For
     calls shorter than their host overhead, graph=True captures the `reps`
     calls once in a HIP graph and times its replays instead (each graph node
     costs a little launch time of its own, so the longer calls are timed
-    eagerly). The first timing of a process is preceded by settle()."""
+    eagerly). The first timing of a process is preceded by settle(); warm_ms
+    > 0 runs fn itself that long first (matrix-core rows: their clock ramps
+    over the first ~30 ms of their own load, whatever ran before)."""
     if not _SETTLED[0]:
         settle(torch, lambda i: fn(i % rotate))
         _SETTLED[0] = True
+    if warm_ms > 0:
+        settle(torch, lambda i: fn(i % rotate), warm_ms)
     g = None
     if graph:
         torch.cuda.synchronize()
@@ -257,7 +264,8 @@ def sec_llm7b(torch, aql, workloads, dev):
             fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
             for i in range(ncopy):
                 fn(i)
-            med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy)
+            med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy,
+                                   warm_ms=0.0 if M <= 16 else 40.0)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N
             gbs = nb / (med * 1e-3) / 1e9
             tf = 2 * M * N * K / (med * 1e-3) / 1e12
@@ -295,7 +303,7 @@ def sec_q8ta(torch, aql, workloads, dev):
                                                  two, s2, 0, y, wsb)
         for i in range(ncopy):
             fn(i)
-        med, _ = event_time_ms(torch, fn, 40, ncopy)
+        med, _ = event_time_ms(torch, fn, 40, ncopy, warm_ms=40.0)
         pro = lambda i: aql.aql_quantize_act_per_tensor(x, s1, z1, two, s2, 0, xq1, xq2)
         pmed, _ = event_time_ms(torch, pro, 40, 1, graph=True)
         ops = (2 if two else 1) * 2 * M * N * K
@@ -328,7 +336,8 @@ def sec_dq8ca(torch, aql, workloads, dev):
                                             None, y, workspace=wsb)
         for i in range(ncopy):
             fn(i)
-        med, _ = event_time_ms(torch, fn, 20 if M > 1000 else 40, ncopy)
+        med, _ = event_time_ms(torch, fn, 20 if M > 1000 else 40, ncopy,
+                               warm_ms=40.0 if M > 16 else 0.0)
         ops = 2 * M * N * K
         nb = N * K // 2 + 4 * gs.numel() + 4 * M * K + 4 * M * N + 8 * M
         rows.append({"workload": f"dq8ca_8da4w M={M} K={K} N={N}", "us": med * 1e3,
@@ -412,7 +421,7 @@ def sec_gptq(torch, aql, workloads, dev):
         torch.cuda.synchronize()
         if int(info.cpu()[0]) != 0:
             raise RuntimeError(f"gptq {name}: info {int(info.cpu()[0])}")
-        med, _ = event_time_ms(torch, fn, 3, 1, trials=3)
+        med, _ = event_time_ms(torch, fn, 3, 1, trials=3, warm_ms=40.0)
         fl = gptq_flops(N, K, 128)
         row = {"workload": f"gptq_int8 {name} K={K} N={N} block=128 (fp64)", "ms": med,
                "TFLOP/s": fl / (med * 1e-3) / 1e12,

@@ -369,6 +369,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
           b[j] = nib_bf16x8(w);
           gsv[j] = *reinterpret_cast<const float *>(st + C::G_OFF + R * 16 + 4 * gg);
         }
+        __builtin_amdgcn_s_setprio(1);  // MFMA run at raised wave priority
 #pragma unroll
         for (int i = 0; i < TI; ++i)
           corr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bneg, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -380,6 +381,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
 #pragma unroll
             for (int v = 0; v < 4; ++v) f[i][j][v] = __builtin_fmaf(gsv[j], t[v], f[i][j][v]);
           }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
   };

@@ -405,11 +405,11 @@ def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
     check_float(y, o["y"], o["tol"], FP32, f"dq8ca {wfmt} {M}x{N}x{K}")
 
 
-def test_dq8ca_q4_large_tiles_ragged():
-    """Enough rows and columns for the 128 x 128 tiles of the 4-bit kernel, with
-    ragged edges in M and N and an odd number of groups (the last 64-k stage
-    holds one group)."""
-    M, N, K = 2000, 4100, 96
+@pytest.mark.parametrize("M,N,K", [(2000, 4100, 96), (1500, 4100, 160)])
+def test_dq8ca_q4_large_tiles_ragged(M, N, K):
+    """Enough rows and columns for the 128 x 128 tiles (2000 x 4100) and the
+    64 x 64 tiles (1500 x 4100) of the 4-bit kernel, with ragged edges in M
+    and N and an odd number of groups (the last 64-k stage holds one group)."""
     say("dq8ca q4 large ragged", M, N, K)
     g = workloads.gen(650)
     x = _edge_rows(workloads.small_matrix(g, M, K))

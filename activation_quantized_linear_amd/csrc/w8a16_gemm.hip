@@ -250,25 +250,30 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
 // instead of 24 KB for half that. Each wave widens only its own 32 channels
 // and uses every widened fragment for 8 MFMAs; with 2 x 4 waves of 64 x 64 the
 // widening was done twice and took ~20% longer.
+template <int SG>
 struct WideLds {
   static constexpr int BM = 128, BNW = 256;
   static constexpr int XS = BM * 128;           // x stage: 128 rows x 64 bf16
   static constexpr int WS = BNW * 64;           // weight stage: 256 rows x 64 int8
   static constexpr int STAGE = XS + WS;         // 32 KB
-  static constexpr int RING = STAGES * STAGE;   // 128 KB
+  static constexpr int RING = SG * STAGE;       // SG stages of 32 KB
   static constexpr int TLD = BNW + 8;           // bf16 per staged output row
   static constexpr int TILE = BM * TLD * 2;
   static constexpr int BYTES = RING > TILE ? RING : TILE;
 };
 
-__global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restrict__ x,
+// SG = 4: a 4-stage ring, one workgroup a CU. SG = 2: a 2-stage ring in
+// 64 KB, so two workgroups share a CU and each covers the other's waits at
+// the stage barrier (from 512 tiles on, where every CU gets two).
+template <int SG>
+__global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const uint16_t *__restrict__ x,
                                                          const int8_t *__restrict__ q,
                                                          const float *__restrict__ scale,
                                                          const uint16_t *__restrict__ bias,
                                                          uint16_t *__restrict__ y, int64_t M,
                                                          int64_t N, int64_t K, int tiles_m,
                                                          int tiles_n) {
-  using L = WideLds;
+  using L = WideLds<SG>;
   constexpr int BM = L::BM, BNW = L::BNW, NL = 4;  // loads per wave per stage
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
   auto issue = [&](int kt) {
 #pragma unroll
     for (int qq = 0; qq < NL; ++qq) {
-      const uint32_t dst = lds_base + (uint32_t)((kt % STAGES) * L::STAGE) + ldso[qq];
+      const uint32_t dst = lds_base + (uint32_t)((kt % SG) * L::STAGE) + ldso[qq];
       const int o = kt < kin_lim[qq] ? (int)(off[qq] + kstep[qq] * (uint32_t)kt) : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           qq < 2 ? rx : rq, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16, o, 0,
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int kt) {
-    const char *st = smem + (kt % STAGES) * L::STAGE;
+    const char *st = smem + (kt % SG) * L::STAGE;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 fa[8], fb[2];
@@ -371,27 +376,31 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
 
   const int nk = (int)((K + BK - 1) / BK);
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  for (int s = 0; s < SG - 1; ++s) issue(s);
   int kt = 0;
   auto step = [&](int k) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (SG - 2)));
     __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
-    issue(k + STAGES - 1);
+    issue(k + SG - 1);
     compute(k);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this stage's fragment reads done
   };
-  // whole turns of the ring first: each stage's LDS offsets become constants
-  const int nmain = nk - (STAGES - 1);
-  for (; kt + STAGES - 1 < nmain; kt += STAGES) {
+  const int nmain = nk - (SG - 1);
+  if constexpr (SG == 4) {
+    // whole turns of the ring first: each stage's LDS offsets become
+    // constants (the 2-stage ring keeps its loop rolled: within the register
+    // budget of two workgroups a CU the unrolled loop spills)
+    for (; kt + SG - 1 < nmain; kt += SG) {
 #pragma unroll
-    for (int u = 0; u < STAGES; ++u) step(kt + u);
+      for (int u = 0; u < SG; ++u) step(kt + u);
+    }
   }
   for (; kt < nmain; ++kt) step(kt);
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t) {
+  for (int t = 0; t < SG - 1; ++t) {
     if (kt < nk) {
-      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 3)));
+      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (SG - 2)));
+      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (SG > 3 ? NL * (SG - 3) : 0));
       else __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       compute(kt);
@@ -437,19 +446,20 @@ __global__ __launch_bounds__(512) void k_w8a16_gemm_wide(const uint16_t *__restr
   }
 }
 
+template <int SG>
 hipError_t launch_wide(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
                        const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
-  using L = WideLds;
+  using L = WideLds<SG>;
   static bool attr_set = false;
   if (!attr_set) {  // more than 64 KB of dynamic LDS; a launch the limit refuses reports itself
-    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide,
+    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide<SG>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     (void)hipGetLastError();
     attr_set = true;
   }
   const int tiles_m = (int)((M + L::BM - 1) / L::BM), tiles_n = (int)((N + L::BNW - 1) / L::BNW);
-  hipLaunchKernelGGL(k_w8a16_gemm_wide, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), L::BYTES,
-                     st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL(k_w8a16_gemm_wide<SG>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512),
+                     L::BYTES, st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -473,13 +483,14 @@ hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, c
 }  // namespace
 
 // 128 x 256 tiles from 160 of them on (fewer than one per CU still beats the
-// smaller tiles' extra round), else 128 x 128 tiles when those fill the CUs,
-// else 64 x 128 tiles.
+// smaller tiles' extra round), two workgroups a CU from 512 on; else 128 x 128
+// tiles when those fill the CUs, else 64 x 128 tiles.
 hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                              hipStream_t st) {
-  const int64_t twide = ((M + WideLds::BM - 1) / WideLds::BM) * ((N + WideLds::BNW - 1) / WideLds::BNW);
-  if (twide >= 160) return launch_wide(x, M, K, q, scale, bias, N, y, st);
+  const int64_t twide = ((M + 127) / 128) * ((N + 255) / 256);
+  if (twide >= 512) return launch_wide<2>(x, M, K, q, scale, bias, N, y, st);
+  if (twide >= 160) return launch_wide<4>(x, M, K, q, scale, bias, N, y, st);
   const int64_t t128 = ((M + 127) / 128) * ((N + BN - 1) / BN);
   if (t128 >= 256) return launch_wm<2>(x, M, K, q, scale, bias, N, y, st);
   return launch_wm<1>(x, M, K, q, scale, bias, N, y, st);

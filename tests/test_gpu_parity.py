@@ -280,12 +280,13 @@ def test_w8a16_smolvlm_sweep():
 
 @pytest.mark.parametrize("M,N,K", [(64, 128, 64), (65, 129, 80), (128, 300, 1040), (200, 257, 4096),
                                    (513, 130, 272), (1024, 2048, 512), (2000, 4100, 272),
-                                   (1920, 8200, 80)])
+                                   (1920, 8200, 80), (2100, 8200, 144)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_prefill_shapes(M, N, K, with_bias):
     """Prefill-sized M runs the tiled bf16-MFMA GEMM (64 x 128, 128 x 128 or,
-    from 256 tiles on, 128 x 256 tiles): ragged M, N and K (K % 64 != 0), N
-    not a multiple of 8, with and without bias."""
+    from 160 tiles on, 128 x 256 tiles, with a 2-stage ring from 512 on):
+    ragged M, N and K (K % 64 != 0), N not a multiple of 8, with and without
+    bias."""
     say("w8a16 prefill", M, N, K, with_bias)
     g = workloads.gen(700 + M + N + K)
     w = workloads.small_matrix(g, N, K, std=0.02)

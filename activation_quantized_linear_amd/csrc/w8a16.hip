@@ -690,7 +690,8 @@ bool m1_shape_ok(const W8A16Shape &sh) {
 // Launch shape, from a sweep of tile rows x waves on the 7B MLP shapes and the
 // SmolVLM decode sweep: streaming is fastest with few waves per workgroup and
 // enough wave-tiles in flight: for the single-row tile about 3000 (8-channel
-// tiles; waves split K only while the tiles alone fall short), for larger M
+// tiles; waves split K only while the tiles alone fall short; about 1000 for
+// rows of 8 KiB and more, measured on K = 8192, 12288 and 14336), for larger M
 // about 768 (8-channel tiles for M <= 2, 16 otherwise). The single-row tile
 // reads x from LDS whenever 2 K fits the budget (one 1 KiB load per wave
 // instruction instead of 512 bytes per step and wave), and pairs wave tiles in
@@ -715,13 +716,17 @@ W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K) {
   s.mblocks = M == 1 ? 0 : (M <= 4 ? 1 : (M <= 8 ? 2 : 4));
   s.tgroups = M <= 2 ? 2 : 4;
   const int64_t tiles = ((N + 4 * s.tgroups - 1) / (4 * s.tgroups)) * ((M + 15) / 16);
-  const int64_t want = M == 1 ? 3072 : 768;
+  // long rows (K >= 8 KiB) stream best from fewer, longer waves (~1024 wave
+  // tiles), with two wave tiles sharing a workgroup's copy of x once waves
+  // split K
+  const bool long_k = M == 1 && nst >= 32;
+  const int64_t want = M == 1 ? (long_k ? 1024 : 3072) : 768;
   const int wmax = M == 1 ? 8 : 16;
   int W = 1;
   while (W < wmax && tiles * W < want && W * (M == 1 ? 2 : 4) <= nst) W <<= 1;
   s.waves = W;
   if (M == 1) {
-    s.cgroups = tiles * W >= 8192 ? 2 : 1;
+    s.cgroups = long_k ? (W >= 2 ? 2 : 1) : (tiles * W >= 8192 ? 2 : 1);
     s.xlds = w8a16_xlds_bytes(K);
   }
   return s;

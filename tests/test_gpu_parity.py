@@ -218,7 +218,8 @@ def test_w8a16_tiny():
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 15, 80), (1, 100, 960), (3, 33, 2560),
                                    (16, 64, 4112), (17, 50, 128), (33, 129, 256), (70, 40, 1024),
                                    (1, 9, 272), (1, 70, 16384), (1, 37, 16400), (1, 200, 20000),
-                                   (1, 4100, 48), (1, 70001, 32)])
+                                   (1, 4100, 48), (1, 70001, 32), (1, 1000, 8208),
+                                   (1, 4100, 12288)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_shapes(M, N, K, with_bias):
     say("w8a16", M, N, K, with_bias)

@@ -281,7 +281,8 @@ def test_w8a16_smolvlm_sweep():
 
 @pytest.mark.parametrize("M,N,K", [(64, 128, 64), (65, 129, 80), (128, 300, 1040), (200, 257, 4096),
                                    (513, 130, 272), (1024, 2048, 512), (2000, 4100, 272),
-                                   (1920, 8200, 80), (2100, 8200, 144)])
+                                   (1920, 8200, 80), (2100, 8200, 144), (2000, 4100, 16),
+                                   (2100, 8200, 48)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_prefill_shapes(M, N, K, with_bias):
     """Prefill-sized M runs the tiled bf16-MFMA GEMM (64 x 128, 128 x 128 or,

@@ -5,15 +5,17 @@
 // on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation) with
 // the weights widened in registers, and the scale is applied once per output.
 //
-// Tile: BM (64 or 128) rows of x x 128 output channels per workgroup. Waves are
-// (BM / 64) x 2 quadrants of 64 x 64 (4 x 4 MFMA tiles each) times 2 halves of
-// every 64-k stage; the halves' fp32 accumulators are added once at the end.
+// Tiles: on large grids 128 rows of x x 256 output channels per workgroup of 8
+// waves side by side along N (k_w8a16_gemm_wide, below); otherwise BM (64 or
+// 128) rows x 128 channels, waves (BM / 64) x 2 quadrants of 64 x 64 (4 x 4
+// MFMA tiles each) times 2 halves of every 64-k stage, the halves' fp32
+// accumulators added once at the end.
 // Operands go global -> LDS by buffer loads that write LDS directly (hardware
 // zero-fill past M, N and K): x as bf16 rows of 128 B, the weights as int8 rows
 // of 64 B (half the bytes of bf16; they are widened after the fragment read).
-// A 4-stage ring keeps three stages in flight behind exact vmcnt waits and a
-// fence-free barrier (a straight-line loop, so the compiler's wait counts stay
-// exact). x rows store their 16-byte chunks XOR-swizzled by (row / 2) mod 8 and
+// A 4-stage ring (2 stages for the wide tile on the largest grids) keeps the
+// next stages in flight behind exact vmcnt waits and a fence-free barrier (a
+// straight-line loop, so the compiler's wait counts stay exact). x rows store their 16-byte chunks XOR-swizzled by (row / 2) mod 8 and
 // weight rows by (row / 4) mod 4, which makes every fragment read conflict-free.
 // The output tile is staged in LDS as bf16 and written as whole rows.
 #include "common.h"

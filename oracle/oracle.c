@@ -15,9 +15,10 @@
  *
  * Plain and slow on purpose: every function is the definition on the pages
  * written out in loops, in the order the pages state it. OpenMP splits only
- * independent output rows, so no result depends on the thread count (the
- * SmolVLM recipe's RefSDPA note: sums whose order follows the thread split
- * change from run to run). Integer sums are int64; float references are
+ * independent outputs (rows, or the (row, column) pairs of the linears), and
+ * every sum runs whole inside one thread, so no result depends on the thread
+ * count (the SmolVLM recipe's RefSDPA note: sums whose order follows the
+ * thread split change from run to run). Integer sums are int64; float references are
  * fp64 sums of exact products.
  *
  * Citations name the page and the section on it:
@@ -265,7 +266,7 @@ int orc_gemm_i8_i64(const int8_t *a, const int8_t *b, int64_t M, int64_t N,
                     int64_t K, int64_t *c)
 {
     if (M < 0 || N < 0 || K < 0) return ORC_BAD;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             int64_t acc = 0;
@@ -294,7 +295,7 @@ int orc_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      double *y, double *tol)
 {
     if (M < 0 || N < 0 || K < 0) return ORC_BAD;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
@@ -322,7 +323,7 @@ int orc_linear_w8a16_dequant_first(const uint16_t *x, int64_t M, int64_t K,
                                    const uint16_t *bias, int64_t N, double *y)
 {
     if (M < 0 || N < 0 || K < 0) return ORC_BAD;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;
@@ -366,7 +367,7 @@ int orc_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1,
     int rc = orc_quantize_act_per_tensor(x, M * K, s1, z1, two_pass, s2, z2, xq1,
                                          two_pass ? xq2 : NULL);
     if (rc != ORC_OK) { free(xq1); free(xq2); return rc; }
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             int64_t acc1 = 0, acc2 = 0, ws = 0;
@@ -415,7 +416,7 @@ int orc_linear_q8ta_dequant_first(const int8_t *xq1, const int8_t *xq2,
                                   const float *bias, int64_t N, double *y)
 {
     if (M < 0 || N < 0 || K < 0) return ORC_BAD;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double y1 = 0.0, y2 = 0.0;
@@ -461,7 +462,7 @@ int orc_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt,
     if (!s || !z || !xq) { free(s); free(z); free(xq); return ORC_BAD; }
     orc_choose_qparams_rows(x, M, K, s, z, xq);
     const int64_t G = (wfmt == 1) ? K / group : 1;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0, mag = 0.0;
@@ -522,7 +523,7 @@ int orc_linear_dq8ca_dequant_first(const int8_t *xq, const float *xs,
 {
     if (M < 0 || N < 0 || K <= 0) return ORC_BAD;
     const int64_t G = (wfmt == 1) ? K / group : 1;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; ++m) {
         for (int64_t n = 0; n < N; ++n) {
             double acc = 0.0;

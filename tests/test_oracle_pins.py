@@ -369,10 +369,12 @@ def _calib(rows):
     return float(s), z
 
 
-@pytest.mark.parametrize("two_pass", [False, True])
-def test_q8ta_matches_q8linear_forward(two_pass):
+@pytest.mark.parametrize("two_pass,z2", [(False, 0), (True, 0), (True, -5), (True, 7)])
+def test_q8ta_matches_q8linear_forward(two_pass, z2):
     """SmolVLM recipe Q8Linear.forward, run with torch's quantized_decomposed ops
-    and F.linear in fp64, against the oracle's int-accumulate-then-scale form."""
+    and F.linear in fp64, against the oracle's int-accumulate-then-scale form.
+    The second pass takes its own affine pair (s2, z2): with z2 != 0 the fold
+    acc2 - z2 * wsum must reproduce dequantize (r1q - z2) * s2."""
     d = workloads.two_pass(seed=5, M=24, K=256, N=40)
     x, w = d["x"], d["w"]
     s1, z1 = _calib(x[1:].numpy())
@@ -380,7 +382,7 @@ def test_q8ta_matches_q8linear_forward(two_pass):
     q, ws, _ = oracle.quantize_weight_int8(w.numpy(), 1)
     g = workloads.gen(50)
     bias = workloads.small_matrix(g, 1, 40)[0].numpy()
-    o = oracle.linear_q8ta_q8csw(x.numpy(), s1, z1, q, ws, bias, two_pass, s2, 0)
+    o = oracle.linear_q8ta_q8csw(x.numpy(), s1, z1, q, ws, bias, two_pass, s2, z2)
     qt = torch.from_numpy(q)
     wt = qd.dequantize_per_channel(qt, torch.from_numpy(ws), torch.zeros(40, dtype=torch.int64),
                                    0, -128, 127, torch.int8).double()
@@ -390,14 +392,14 @@ def test_q8ta_matches_q8linear_forward(two_pass):
     y = torch.nn.functional.linear(x1, wt, torch.from_numpy(bias).double())
     if two_pass:
         r = x - (torch.clamp(torch.round(x * (1.0 / s1)) + z1, -128, 127) - z1) * s1
-        r1q = qd.quantize_per_tensor(r, s2, 0, -128, 127, torch.int8)
+        r1q = qd.quantize_per_tensor(r, s2, z2, -128, 127, torch.int8)
         assert np.array_equal(r1q.numpy(), o["xq2"])
-        r1 = r1q.double() * np.float64(np.float32(s2))
+        r1 = (r1q.double() - z2) * np.float64(np.float32(s2))
         y = y + torch.nn.functional.linear(r1, wt)
     # dequantize_per_channel returns fp32 weights: q * ws is rounded once (2^-24)
     assert np.all(np.abs(y.numpy() - o["y"]) <= 2.0**-23 * o["tol"])
     y2 = oracle.linear_q8ta_dequant_first(o["xq1"], o["xq2"], s1, z1, q, ws, bias, two_pass,
-                                          s2, 0)
+                                          s2, z2)
     assert np.all(np.abs(y2 - o["y"]) <= 1e-12 * o["tol"])
     acc = oracle.gemm_i8(o["xq1"], q)
     assert np.array_equal(acc, o["acc1"])

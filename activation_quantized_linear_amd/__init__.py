@@ -38,6 +38,7 @@ AQL_OP_Q8TA_Q8CSW = 1
 AQL_OP_DQ8CA = 2
 AQL_OP_GPTQ_INT8 = 3
 AQL_MAX_K_INT8 = 65536
+AQL_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run python -c 'import __graft_entry__ as g; "
@@ -64,6 +65,8 @@ _SIGS = {
     "aql_linear_w8a16": ([_p, _i64, _i64, _p, _p, _p, _i64, _p, _p], _int),
     "aql_linear_q8ta_q8csw": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p, _p, _p,
                                _i64, _p, _p, _sz, _p], _int),
+    "aql_linear_q8ta_q8csw_noalloc": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p,
+                                       _p, _p, _i64, _p, _p], _int),
     "aql_linear_dq8ca": ([_p, _i64, _i64, _int, _p, _p, _p, _int, _p, _i64, _p, _p, _p, _p, _sz,
                           _p], _int),
     "aql_gemm_i8_i32": ([_p, _p, _p, _i64, _i64, _i64, _p], _int),
@@ -270,6 +273,33 @@ def aql_linear_q8ta_q8csw(x, s1, z1, q, wsum, wscale, bias=None, two_pass=False,
                                       float(s2), int(z2), _ptr(q), _ptr(wsum), _ptr(wscale),
                                       _ptr(bias), N, _ptr(y), _ptr(ws), ws.numel(),
                                       _stream(dev)))
+    return y
+
+
+def aql_linear_q8ta_q8csw_noalloc(x, s1, z1, q, wsum, wscale, bias=None, two_pass=False, s2=1.0,
+                                  z2=0, y=None):
+    """aql_linear_q8ta_q8csw on the library's fixed per-GPU scratch (no workspace
+    argument; the C entry allocates nothing). Pass y to allocate nothing here
+    either. Calls that overlap on one GPU race on the shared scratch."""
+    _need(x, "x", torch.float32, 2)
+    dev = x.device
+    M, K = x.shape
+    _need(q, "q", torch.int8, 2, dev)
+    N = q.shape[0]
+    _shape(q, "q", (N, K))
+    _need(wsum, "wsum", torch.int32, 1, dev)
+    _shape(wsum, "wsum", (N,))
+    _need(wscale, "wscale", torch.float32, 1, dev)
+    _shape(wscale, "wscale", (N,))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, 1, dev)
+        _shape(bias, "bias", (N,))
+    y = _out(y, "y", (M, N), torch.float32, dev)
+    _check("aql_linear_q8ta_q8csw_noalloc",
+           _lib.aql_linear_q8ta_q8csw_noalloc(_ptr(x), M, K, float(s1), int(z1),
+                                              int(bool(two_pass)), float(s2), int(z2), _ptr(q),
+                                              _ptr(wsum), _ptr(wscale), _ptr(bias), N, _ptr(y),
+                                              _stream(dev)))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -128,6 +129,87 @@ int check_w8a16(const char *fn, const uint16_t *x, int64_t M, int64_t K, const i
           AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return AQL_OK;
   REQUIRE(x && q && scale && y, AQL_ERR_NULL, "%s: x, q, scale and y must not be NULL", fn);
+  return AQL_OK;
+}
+
+// Validation shared by both static W8A8 entry points (all before any HIP call).
+int check_q8ta(const char *fn, const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+               int two_pass, float s2, int32_t z2, const int8_t *q, const int32_t *wsum,
+               const float *wscale, const float *bias, int64_t N, const float *y) {
+  REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
+          "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
+  REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
+          "%s: s2 must be finite and > 0, z2 in [-128, 127]", fn);
+  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
+          "%s: need M, N >= 0 and K a multiple of 16 in [16, %d] (M=%lld N=%lld K=%lld)", fn,
+          AQL_MAX_K_INT8, (long long)M, (long long)N, (long long)K);
+  REQUIRE(M < (1LL << 31) / 128 && N < (1LL << 31) / 128, AQL_ERR_SHAPE, "%s: M or N too large",
+          fn);
+  REQUIRE(aligned16(x) && aligned16(q) && aligned16(wsum) && aligned16(wscale) &&
+              aligned16(bias) && aligned16(y),
+          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (M == 0 || N == 0) return AQL_OK;
+  REQUIRE(x && q && wsum && wscale && y, AQL_ERR_NULL,
+          "%s: x, q, wsum, wscale and y must not be NULL", fn);
+  return AQL_OK;
+}
+
+// The static W8A8 linear on a validated call: the activation quantizer writes
+// xq1 (and xq2) into ws, then the int8 GEMM with the fused epilogue. Every
+// byte of ws that the GEMM reads is written by the quantizer first, so ws
+// needs no clearing.
+int run_q8ta(const char *fn, const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+             int two_pass, float s2, int32_t z2, const int8_t *q, const int32_t *wsum,
+             const float *wscale, const float *bias, int64_t N, float *y, void *ws,
+             hipStream_t st) {
+  int8_t *xq1 = static_cast<int8_t *>(ws);
+  int8_t *xq2 = xq1 + align256((size_t)M * (size_t)K);
+  hipError_t e = aql::launch_quantize_act_per_tensor(x, M * K, s1, z1, two_pass != 0, s2, z2, xq1,
+                                                     xq2, st);
+  if (e != hipSuccess) return launched(e, fn);
+  aql::GemmArgs a{};
+  a.a1 = xq1;
+  a.a2 = xq2;
+  a.b = q;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.y = y;
+  a.wsum = wsum;
+  a.wscale = wscale;
+  a.bias = bias;
+  a.s1 = s1;
+  a.s2 = s2;
+  a.z1 = z1;
+  a.z2 = z2;
+  return launched(aql::launch_gemm_i8(a, aql::EPI_Q8TA, two_pass != 0, st), fn);
+}
+
+// Scratch of the allocation-free entry point: a fixed device array that every
+// GPU the library runs on holds until the process ends. Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the
+// symbol); each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is what the kernels are given.
+__device__ __align__(256) unsigned char scratch[AQL_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device index (check_device bounds it to 64)
+
+int scratch_of_current_device(const char *fn, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64)
+    return fail(AQL_ERR_DEVICE, "%s: no usable HIP device", fn);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(AQL_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed on device "
+                  "%d (%s)", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return AQL_OK;
 }
 
@@ -347,47 +429,36 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
                           const int32_t *wsum, const float *wscale, const float *bias, int64_t N,
                           float *y, void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "aql_linear_q8ta_q8csw";
-  REQUIRE(finite_pos(s1) && z_ok(z1), AQL_ERR_PARAM,
-          "%s: s1 must be finite and > 0, z1 in [-128, 127]", fn);
-  REQUIRE(!two_pass || (finite_pos(s2) && z_ok(z2)), AQL_ERR_PARAM,
-          "%s: s2 must be finite and > 0, z2 in [-128, 127]", fn);
-  REQUIRE(M >= 0 && N >= 0 && K >= 16 && K % 16 == 0 && K <= AQL_MAX_K_INT8, AQL_ERR_SHAPE,
-          "%s: need M, N >= 0 and K a multiple of 16 in [16, %d] (M=%lld N=%lld K=%lld)", fn,
-          AQL_MAX_K_INT8, (long long)M, (long long)N, (long long)K);
-  REQUIRE(M < (1LL << 31) / 128 && N < (1LL << 31) / 128, AQL_ERR_SHAPE, "%s: M or N too large",
-          fn);
-  REQUIRE(aligned16(x) && aligned16(q) && aligned16(wsum) && aligned16(wscale) &&
-              aligned16(bias) && aligned16(y) && aligned16(ws),
-          AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
+  if (int e = check_q8ta(fn, x, M, K, s1, z1, two_pass, s2, z2, q, wsum, wscale, bias, N, y))
+    return e;
+  REQUIRE(aligned16(ws), AQL_ERR_ALIGN, "%s: pointers must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
-  REQUIRE(x && q && wsum && wscale && y, AQL_ERR_NULL,
-          "%s: x, q, wsum, wscale and y must not be NULL", fn);
   const size_t need = ws_q8ta(M, K);
   REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
           fn, need, ws ? ws_bytes : (size_t)0);
   if (int e = check_device(fn)) return e;
-  int8_t *xq1 = static_cast<int8_t *>(ws);
-  int8_t *xq2 = xq1 + align256((size_t)M * (size_t)K);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = aql::launch_quantize_act_per_tensor(x, M * K, s1, z1, two_pass != 0, s2, z2, xq1,
-                                                     xq2, st);
-  if (e != hipSuccess) return launched(e, fn);
-  aql::GemmArgs a{};
-  a.a1 = xq1;
-  a.a2 = xq2;
-  a.b = q;
-  a.M = M;
-  a.N = N;
-  a.K = K;
-  a.y = y;
-  a.wsum = wsum;
-  a.wscale = wscale;
-  a.bias = bias;
-  a.s1 = s1;
-  a.s2 = s2;
-  a.z1 = z1;
-  a.z2 = z2;
-  return launched(aql::launch_gemm_i8(a, aql::EPI_Q8TA, two_pass != 0, st), fn);
+  return run_q8ta(fn, x, M, K, s1, z1, two_pass, s2, z2, q, wsum, wscale, bias, N, y, ws,
+                  (hipStream_t)stream);
+}
+
+int aql_linear_q8ta_q8csw_noalloc(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                                  int two_pass, float s2, int32_t z2, const int8_t *q,
+                                  const int32_t *wsum, const float *wscale, const float *bias,
+                                  int64_t N, float *y, void *stream) {
+  const char *fn = "aql_linear_q8ta_q8csw_noalloc";
+  if (int e = check_q8ta(fn, x, M, K, s1, z1, two_pass, s2, z2, q, wsum, wscale, bias, N, y))
+    return e;
+  if (M == 0 || N == 0) return ok();
+  const size_t need = ws_q8ta(M, K);
+  REQUIRE(need <= (size_t)AQL_NOALLOC_SCRATCH_BYTES, AQL_ERR_WORKSPACE,
+          "%s: M x K = %lld x %lld needs %zu bytes of scratch, more than the library's fixed "
+          "%d (use aql_linear_q8ta_q8csw with a workspace)",
+          fn, (long long)M, (long long)K, need, AQL_NOALLOC_SCRATCH_BYTES);
+  if (int e = check_device(fn)) return e;
+  void *ws = nullptr;
+  if (int e = scratch_of_current_device(fn, &ws)) return e;
+  return run_q8ta(fn, x, M, K, s1, z1, two_pass, s2, z2, q, wsum, wscale, bias, N, y, ws,
+                  (hipStream_t)stream);
 }
 
 int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void *wq,

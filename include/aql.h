@@ -75,6 +75,10 @@ extern "C" {
 /* Largest K accepted by the int8 paths: keeps |sum_k (xq - z) q| below 2^31. */
 #define AQL_MAX_K_INT8 65536
 
+/* Bytes of the fixed device scratch of aql_linear_q8ta_q8csw_noalloc (8 MiB:
+ * M * K up to 4 Mi elements). */
+#define AQL_NOALLOC_SCRATCH_BYTES (8 << 20)
+
 /* ------------------------------------------------------------------ helpers */
 
 /* Library version, major*10000 + minor*100 + patch. Never fails. */
@@ -214,6 +218,29 @@ int aql_linear_q8ta_q8csw(const float *x, int64_t M, int64_t K, float s1, int32_
                           int two_pass, float s2, int32_t z2, const int8_t *q,
                           const int32_t *wsum, const float *wscale, const float *bias, int64_t N,
                           float *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as aql_linear_q8ta_q8csw, without the
+ * workspace argument. The activation codes go to a fixed scratch array of
+ * AQL_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; nothing is allocated or freed. The caller still
+ * provides x, the weights and y.
+ *   Every call on one GPU shares that GPU's scratch and leaves its codes
+ *   there: calls that overlap on one GPU (on different streams, or from
+ *   different threads) race and give undefined results; calls ordered on one
+ *   stream do not. Results are bit-identical to aql_linear_q8ta_q8csw.
+ * Errors: as aql_linear_q8ta_q8csw; AQL_ERR_WORKSPACE when the call needs
+ * more scratch than AQL_NOALLOC_SCRATCH_BYTES (the workspace size of
+ * aql_linear_q8ta_q8csw: twice M * K rounded up to 256), checked before any
+ * HIP call;
+ * AQL_ERR_HIP if the scratch address cannot be obtained on the device.
+ */
+int aql_linear_q8ta_q8csw_noalloc(const float *x, int64_t M, int64_t K, float s1, int32_t z1,
+                                  int two_pass, float s2, int32_t z2, const int8_t *q,
+                                  const int32_t *wsum, const float *wscale, const float *bias,
+                                  int64_t N, float *y, void *stream);
 
 /*
  * W8A8 linear with dynamic per-row asymmetric int8 activations

@@ -128,6 +128,30 @@ def test_q8ta_validation():
     assert f(*args(M=0)) == aql.AQL_OK
 
 
+def test_q8ta_noalloc_validation():
+    """The allocation-free static W8A8 entry: the same checks as the workspace
+    entry, and a call needing more than the fixed scratch is refused before any
+    HIP call."""
+    f = L.aql_linear_q8ta_q8csw_noalloc
+    args = lambda **k: [k.get("x", A), k.get("M", 4), k.get("K", 64), k.get("s1", 0.1),
+                        k.get("z1", 0), k.get("two", 1), k.get("s2", 0.001), k.get("z2", 0),
+                        k.get("q", B), k.get("wsum", Y), k.get("wsc", Y), None, k.get("N", 8),
+                        k.get("y", Y), None]
+    assert f(*args(q=NUL)) == aql.AQL_ERR_NULL
+    assert f(*args(x=NUL)) == aql.AQL_ERR_NULL
+    assert f(*args(s1=float("inf"))) == aql.AQL_ERR_PARAM
+    assert f(*args(z2=-129)) == aql.AQL_ERR_PARAM
+    assert f(*args(K=40)) == aql.AQL_ERR_SHAPE
+    assert f(*args(x=MIS)) == aql.AQL_ERR_ALIGN
+    # 2 * M * K bytes of codes: 1024 x 4096 fits the 8 MiB exactly, one more row does not
+    assert aql.aql_workspace_bytes(aql.AQL_OP_Q8TA_Q8CSW, 1024, 8, 4096) == \
+        aql.AQL_NOALLOC_SCRATCH_BYTES
+    assert f(*args(M=1025, K=4096)) == aql.AQL_ERR_WORKSPACE
+    assert "scratch" in aql.aql_last_error()
+    assert f(*args(M=0)) == aql.AQL_OK
+    assert f(*args(N=0, M=5000, K=4096)) == aql.AQL_OK  # empty: nothing launched, no scratch
+
+
 def test_dq8ca_validation():
     f = L.aql_linear_dq8ca
     args = lambda **k: [A, k.get("M", 4), k.get("K", 64), k.get("wfmt", 0), B, Y, Y,

@@ -11,6 +11,15 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st);
 
+// Single-row GEMV over contiguous 1 KB row pieces, used by launch_w8a16 for
+// M = 1 and kW8A16ContigMinK <= K <= kW8A16ContigMaxK (measured faster than the
+// 4-row tile there: 10.8 vs 11.3 us at K = 4096, N = 14336; 12.1 vs 12.9 at
+// K = N = 8192; longer rows stream better in the tile's form).
+constexpr int64_t kW8A16ContigMinK = 2048;
+constexpr int64_t kW8A16ContigMaxK = 8192;
+hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const float *scale,
+                            const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st);
+
 // Launch shape of the W8A16 kernel: waves per channel group (they split K),
 // groups of 4 output channels per wave tile (1, 2 or 4) and blocks of 4 rows of
 // x per tile (1, 2 or 4; 0 selects the single-row tile, M = 1; kW8A16Skinny

@@ -57,6 +57,28 @@ __device__ __forceinline__ s16x4 widen4(int w) {
   return __builtin_bit_cast(s16x4, (uint64_t)lo | ((uint64_t)hi << 32));
 }
 
+// Cross-lane sums without LDS: DPP row rotations within a row of 16 lanes,
+// and the gfx950 lane-half swaps across rows (v_permlane16_swap pairs rows
+// 0-1 and 2-3, v_permlane32_swap the two halves of the wave).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor4 = 0x124, kDppRowRor8 = 0x128, kDppRowMirror = 0x140,
+              kDppRowHalfMirror = 0x141, kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E;
+// (a, b) -> a' + b' where lanes 0-31 get a[l] + a[l + 32] and lanes 32-63
+// get b[l - 32] + b[l]: a's pair sum in the low half, b's in the high half.
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// The same across rows of 16: rows 0 and 2 get a's sums with rows 1 and 3,
+// rows 1 and 3 get b's.
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 struct Tile {
   const uint16_t *x;
   const int8_t *q;
@@ -192,12 +214,17 @@ __device__ __forceinline__ void w8a16_tile_m1(const Tile &t, Red<W * CW, TG, 0> 
     b += 2 * U;
   } while (b < cnt);
 
+  // sum the 16 k-slice blocks of column j (lanes j, j + 4, ..., j + 60): two
+  // row rotations, then the two lane-half swaps; every lane ends with its
+  // column's total
   float v[TG];
 #pragma unroll
   for (int tg = 0; tg < TG; ++tg) {
     v[tg] = (acc[tg][0][0] + acc[tg][1][1]) + (acc[tg][2][2] + acc[tg][3][3]);
-#pragma unroll
-    for (int o = 4; o < 64; o <<= 1) v[tg] += __shfl_xor(v[tg], o);
+    v[tg] += dpp_f32<kDppRowRor4>(v[tg]);
+    v[tg] += dpp_f32<kDppRowRor8>(v[tg]);
+    v[tg] = swap16_sum(v[tg], v[tg]);
+    v[tg] = swap32_sum(v[tg], v[tg]);
   }
   if constexpr (W > 1) {
     if (lane < 4) {
@@ -496,6 +523,140 @@ constexpr int batch_steps() {
   return TG * MB <= 8 ? 2 : 1;
 }
 
+// Single-row GEMV for long rows (M = 1, K >= kW8A16ContigMinK), contiguous form.
+// A workgroup owns 8 output channels and its W waves split K into W
+// contiguous ranges (multiples of 16 bytes). A wave reads its range of the 8
+// rows as 1 KB pieces, each one row's 1024 contiguous bytes (64 lanes x 16 B):
+// on gfx950 that streams from HBM faster than the 4 rows x 256 B shape of the
+// other tiles. x for the wave's range comes into registers once, as fp32 (16
+// values per lane and piece), and serves all 8 rows; each weight byte is
+// widened (sign-extending convert) and fused into a per-row fp32 accumulator
+// (int8 x bf16 products are exact in fp32). Loads go in batches of 4 with the
+// next batch in flight while one is used. The 8 rows' lane partials are summed
+// by a transposing butterfly (3 exchange steps halve the values a lane carries,
+// 3 more finish the sum), the waves' sums meet in LDS.
+template <int W, int P, int B = 4>
+__global__ __launch_bounds__(64 * W) void k_w8a16_m1c(const uint16_t *__restrict__ x, int64_t K,
+                                                       const int8_t *__restrict__ q,
+                                                       const float *__restrict__ scale,
+                                                       const uint16_t *__restrict__ bias,
+                                                       int64_t N, uint16_t *__restrict__ y) {
+  constexpr int R = 8;           // channels per workgroup
+  constexpr int NL = R * P;      // weight loads per wave
+  constexpr int NB = (NL + B - 1) / B;
+  __shared__ float red[W][R];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+  const int64_t nrows = N - n0 < R ? N - n0 : R;
+  const int64_t kw = ((K + W - 1) / W + 15) / 16 * 16;
+  const int64_t k0 = wave * kw;
+  const int64_t k1 = K < k0 + kw ? K : k0 + kw;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(q + n0 * K, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)(2 * K));
+
+  // piece p of this wave: lane -> k = k0 + 1024 p + 16 lane .. + 16 (zeros past k1)
+  int kk[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t k = k0 + 1024 * p + 16 * lane;
+    kk[p] = k < k1 ? (int)k : -1;
+  }
+  auto issue = [&](int b, i32x4 *dst) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int L = b * B + u;
+      if (L < NL) {
+        const int r = L % R, p = L / R;
+        const int off = kk[p] >= 0 ? (int)((uint32_t)r * (uint32_t)K + (uint32_t)kk[p]) : OOB;
+        dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 2);
+      }
+    }
+  };
+
+  i32x4 wb0[B], wb1[B];
+  issue(0, wb0);
+  i32x4 xr[P][2];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int off = kk[p] >= 0 ? 2 * kk[p] : OOB;
+    xr[p][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+    xr[p][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off >= 0 && off != OOB ? off + 16 : OOB, 0, 0);
+  }
+  if (NB > 1) issue(1, wb1);
+  float xf[P][16];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t d = (uint32_t)xr[p][h][i];
+        xf[p][8 * h + 2 * i] = __uint_as_float(d << 16);
+        xf[p][8 * h + 2 * i + 1] = __uint_as_float(d & 0xffff0000u);
+      }
+
+  float acc[R][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.0f;
+  auto consume = [&](int b, const i32x4 *src) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int L = b * B + u;
+      if (L < NL) {
+        const int r = L % R, p = L / R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int wv = src[u][e];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[r][i & 1] = fmaf((float)(int8_t)(wv >> (8 * i)), xf[p][4 * e + i], acc[r][i & 1]);
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    __builtin_amdgcn_sched_barrier(0);
+    consume(b, (b & 1) ? wb1 : wb0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 2 < NB) issue(b + 2, (b & 1) ? wb1 : wb0);
+  }
+
+  // transposing butterfly: the lane-half swaps leave rows 0-3 in the low half
+  // and 4-7 in the high half (4 values each), then 2 per row pair, and a row
+  // mirror 1 (the row of lane >> 3); half mirror and two quad exchanges
+  // finish the sum over the 8 lanes of that row
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = acc[r][0] + acc[r][1];
+  float t4[4], t2[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t4[j] = swap32_sum(v[j], v[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) t2[j] = swap16_sum(t4[j], t4[2 + j]);
+  const bool h3 = lane & 8;
+  float sum = (h3 ? t2[1] : t2[0]) + dpp_f32<kDppRowMirror>(h3 ? t2[0] : t2[1]);
+  sum += dpp_f32<kDppRowHalfMirror>(sum);
+  sum += dpp_f32<kDppQuadXor2>(sum);
+  sum += dpp_f32<kDppQuadXor1>(sum);
+  if constexpr (W > 1) {
+    if ((lane & 7) == 0) red[wave][lane >> 3] = sum;
+    __syncthreads();
+    if (wave != 0 || lane >= R) return;
+    sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][lane];
+  } else {
+    if ((lane & 7) != 0) return;
+  }
+  const int row = W > 1 ? lane : lane >> 3;
+  const int64_t n = n0 + row;
+  if (n >= N) return;
+  const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+  y[n] = f32_to_bf16_rne(scale[n] * sum + bv);
+}
+
 constexpr int M1_TG = 2;  // single-row tile: 8 channels per wave tile
 constexpr int M1_U = 2;   // steps per fetched batch
 
@@ -765,9 +926,23 @@ hipError_t launch_w8a16_shape(const W8A16Shape &sh, const uint16_t *x, int64_t M
   return hipGetLastError();
 }
 
+hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const float *scale,
+                            const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
+  if (K < kW8A16ContigMinK || K > kW8A16ContigMaxK || K % 16) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + 7) / 8));
+  // 4 waves split K, each with one or two pieces of 1 KB per row
+  if (K <= 4096)
+    hipLaunchKernelGGL((k_w8a16_m1c<4, 1>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
+  else
+    hipLaunchKernelGGL((k_w8a16_m1c<4, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st) {
+  if (M == 1 && K >= kW8A16ContigMinK && K <= kW8A16ContigMaxK)
+    return launch_w8a16_m1c(x, K, q, scale, bias, N, y, st);
   return launch_w8a16_shape(w8a16_shape(M, N, K), x, M, K, q, scale, bias, N, y, st);
 }
 

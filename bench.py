@@ -150,6 +150,26 @@ def settle(torch, fn, gpu_ms=50.0):
     return i
 
 
+def raw_call(aql, torch, name, argsets):
+    """fn(i) calling the C entry point `name` directly with the i-th prebuilt
+    ctypes argument tuple (device pointers, sizes, the current stream): the
+    same launch as the binding's, without its per-call checks, so that for
+    calls of ~10 us the host stays ahead of the GPU and events time the GPU."""
+    import ctypes as C
+    f = getattr(aql._lib, name)
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def conv(a):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            return C.c_void_p(a.data_ptr())
+        return a
+
+    built = [tuple(conv(a) for a in args) + (st,) for args in argsets]
+    return lambda i: f(*built[i])
+
+
 def copies_for(nbytes, minimum=2):
     return max(minimum, -(-2 * MALL_BYTES // max(nbytes, 1)))
 
@@ -264,6 +284,9 @@ def sec_llm7b(torch, aql, workloads, dev):
             fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
             for i in range(ncopy):
                 fn(i)
+            if M <= 16:  # short calls: the C entry point with prebuilt arguments
+                fn = raw_call(aql, torch, "aql_linear_w8a16",
+                              [(x, M, K, qs[i], s, None, N, y) for i in range(ncopy)])
             med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy,
                                    warm_ms=0.0 if M <= 16 else 40.0)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N
@@ -336,6 +359,10 @@ def sec_dq8ca(torch, aql, workloads, dev):
                                             None, y, workspace=wsb)
         for i in range(ncopy):
             fn(i)
+        if M <= 16:  # short calls: the C entry point with prebuilt arguments
+            fn = raw_call(aql, torch, "aql_linear_dq8ca",
+                          [(x, M, K, aql.AQL_W_Q4GSW, ws[i][0], ws[i][1], ws[i][2], 32, None, N,
+                            y, None, None, wsb, wsb.numel()) for i in range(ncopy)])
         med, _ = event_time_ms(torch, fn, 20 if M > 1000 else 40, ncopy,
                                warm_ms=40.0 if M > 16 else 0.0)
         ops = 2 * M * N * K
@@ -633,7 +660,8 @@ def ceilings(torch, aql, dev):
     del bufs
     n7 = 56 << 20
     bufs = [torch.full((n7,), 1, dtype=torch.uint8, device=dev) for _ in range(10)]
-    rd7_ms, _ = event_time_ms(torch, lambda i: aql.aql_measure_read(bufs[i], sink), 50, 10)
+    rd7 = raw_call(aql, torch, "aql_measure_read", [(b, n7, sink) for b in bufs])
+    rd7_ms, _ = event_time_ms(torch, rd7, 50, 10)
     del bufs
     rd7 = n7 / (rd7_ms * 1e-3) / 1e9
     iters = 20000

@@ -487,14 +487,14 @@ int aql_linear_dq8ca(const float *x, int64_t M, int64_t K, int wfmt, const void 
   REQUIRE(ws && ws_bytes >= need, AQL_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)",
           fn, need, ws ? ws_bytes : (size_t)0);
   if (int e = check_device(fn)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  const bool q4 = wfmt == AQL_W_Q4GSW;
   char *base = static_cast<char *>(ws);
   const size_t xbytes = align256(2 * (size_t)M * (size_t)K);
   int8_t *xq = reinterpret_cast<int8_t *>(base);
   float *xs = x_scale_out ? x_scale_out : reinterpret_cast<float *>(base + xbytes);
   int32_t *xz = x_zp_out ? x_zp_out
                          : reinterpret_cast<int32_t *>(base + xbytes + align256((size_t)M * 4));
-  hipStream_t st = (hipStream_t)stream;
-  const bool q4 = wfmt == AQL_W_Q4GSW;
   const aql::QpOut mode = !q4 ? aql::QP_CODES
                               : (M <= aql::kQ4StreamMaxM ? aql::QP_CODES_PERM8 : aql::QP_DIFF_BF16);
   hipError_t e = aql::launch_choose_qparams_rows(x, M, K, xs, xz, xq, mode, st);

@@ -11,6 +11,10 @@ namespace aql {
 // xq in the permute8 order, larger M the bf16 differences xd (see
 // launch_choose_qparams_rows).
 constexpr int64_t kQ4StreamMaxM = 16;
+// M <= kQ4FewMaxM and K <= kQ4FewMaxK: the few-rows kernel (dot4 group sums,
+// contiguous weight pieces); the codes are in the permute8 order as well
+constexpr int64_t kQ4FewMaxM = 4;
+constexpr int64_t kQ4FewMaxK = 8192;
 struct Q4Args {
   const int8_t *xq;     // [M, K] int8, permute8 order (M <= 16)
   const uint16_t *xd;   // [M, K] bf16 xq - zp, natural order (M > 16)

@@ -16,6 +16,8 @@
 //
 // Either way every 32-k group's int32 sum is formed exactly by the matrix cores
 // and folded into the fp32 accumulator with its group scale right away.
+#include <float.h>
+
 #include "dq8ca_q4.h"
 
 namespace aql {
@@ -202,6 +204,176 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
       if (mm < p.M) p.y[mm * p.N + n] = p.xs[mm] * (sum[v] * 0.0625f) + bv;
     }
   }
+}
+
+// ------------------------------------------------------- few rows (M <= 4)
+// The weights stream as contiguous 1 KB pieces of one channel's row per wave
+// instruction (lane l holds 32-k group 64 p + l whole), the group scales as
+// 256-byte pieces beside them; all of a wave's pieces are requested before
+// anything else, so the whole stream is in flight from the start. The
+// workgroup copies the M rows of codes (permute8 order, from the qparams
+// kernel) into LDS with buffer-to-LDS loads. Each group's sum is formed exactly
+// by signed 4-way byte dot products (v_dot4_i32_i8) of the codes with the
+// nibbles unpacked as 16 c:
+//     A16 = sum_k xq (16 c) - zp * sum_k (16 c)     (|A16| < 2^24, exact)
+// and folded with one FMA, f += gs * A16; y = s * (f / 16) + bias. A wave owns
+// RW channels over all of K, so it needs no other wave's partial sums; its
+// lanes' partials are summed by a transposing butterfly (each exchange step
+// halves the values a lane carries) of DPP moves and lane-half swaps.
+// (Forming the row qparams inside this kernel instead, in every workgroup,
+// measured slower: 12.5 vs 11.3 us at M = 4, K = 4096, N = 11008.)
+template <int CTRL>
+__device__ __forceinline__ float q4_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// lanes 0-31 get a[l] + a[l + 32], lanes 32-63 get b[l - 32] + b[l]
+__device__ __forceinline__ float q4_swap32_sum(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+// rows 0 and 2 get a's sums with rows 1 and 3, rows 1 and 3 get b's
+__device__ __forceinline__ float q4_swap16_sum(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+template <int W, int RW, int NP>
+__global__ __launch_bounds__(64 * W) void k_dq8ca_q4_few(Q4Args p) {
+  constexpr int V = 4 * RW;  // partial sums per lane: RW channels x 4 rows
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] codes, permute8 order
+  __shared__ float qs_s[4], qs_z[4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t M = p.M, N = p.N, K = p.K, G = K / 32, KB = K / 2;
+  const int64_t n0 = (int64_t)blockIdx.x * (W * RW) + (int64_t)wave * RW;
+  const int64_t rem = N - n0;
+  const int64_t nrows = rem <= 0 ? 0 : (rem < RW ? rem : RW);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(nrows > 0 ? p.q4 + n0 * KB : p.q4, (uint32_t)(nrows * KB));
+  const __amdgpu_buffer_rsrc_t rg = rsrc(nrows > 0 ? p.gs + n0 * G : p.gs, (uint32_t)(nrows * G * 4));
+  i32x4 w[NP][RW];
+  float gsv[NP][RW];
+#pragma unroll
+  for (int pc = 0; pc < NP; ++pc) {
+    const int64_t g = 64LL * pc + lane;
+    const bool gin = g < G;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      w[pc][r] = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, gin ? (int)((uint32_t)r * (uint32_t)KB + 16u * (uint32_t)g) : OOB, 0, 2);
+      gsv[pc][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          rg, gin ? (int)(4u * ((uint32_t)r * (uint32_t)G + (uint32_t)g)) : OOB, 0, 2));
+    }
+  }
+  {
+    const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, (uint32_t)(M * K));
+    const int nch = (int)((M * K + 1023) >> 10);
+    const uint32_t base = (uint32_t)(uintptr_t)xl;
+    for (int c = wave; c < nch; c += W)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + 1024u * c), 16,
+          (int)(16u * lane + 1024u * c), 0, 0, 0);
+    if (wave == 0 && lane < 4) {
+      qs_s[lane] = lane < M ? p.xs[lane] : 0.0f;
+      qs_z[lane] = lane < M ? (float)p.xz[lane] : 0.0f;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
+  }
+  __syncthreads();
+  int zpn[4];
+  float sm[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    zpn[m] = -(int)qs_z[m];
+    sm[m] = qs_s[m];
+  }
+
+  float f[RW][4];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) f[r][m] = 0.0f;
+#pragma unroll
+  for (int pc = 0; pc < NP; ++pc) {
+    const int64_t g = 64LL * pc + lane;
+    i32x4 xv[4][2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // rows past M read row 0 (their sums are never written)
+      const int xo = (g < G ? (int)(32 * g) : 0) + (m < M ? m * (int)K : 0);
+      xv[m][0] = *reinterpret_cast<const i32x4 *>(xl + xo);
+      xv[m][1] = *reinterpret_cast<const i32x4 *>(xl + xo + 16);
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      int wq[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)w[pc][r][e];
+        wq[2 * e] = (int)((u << 4) & 0xF0F0F0F0u);  // k = 8e + 0, 2, 4, 6, as 16 c
+        wq[2 * e + 1] = (int)(u & 0xF0F0F0F0u);     // k = 8e + 1, 3, 5, 7
+      }
+      int gsum16 = 0;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) gsum16 = __builtin_amdgcn_sdot4(0x01010101, wq[d], gsum16, false);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        int acc = 0;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc = __builtin_amdgcn_sdot4(xv[m][d >> 2][d & 3], wq[d], acc, false);
+        // |zp| <= 128 and |gsum16| <= 4096: a 24-bit product
+        f[r][m] += gsv[pc][r] * (float)(acc + __mul24(zpn[m], gsum16));
+      }
+    }
+  }
+
+  // ---- sum the V = 4 RW partials over the 64 lanes: log2(V) transposing
+  // exchange steps (lane bits 5, 4, 3, ...), then plain ones; lane l ends with
+  // value index l >> (6 - log2 V)
+  float t[V];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) t[4 * r + m] = f[r][m];
+  static_assert(V == 8 || V == 16 || V == 32, "RW in {2, 4, 8}");
+  constexpr int LV = V == 8 ? 3 : (V == 16 ? 4 : 5);
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) t[j] = q4_swap32_sum(t[j], t[V / 2 + j]);
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) t[j] = q4_swap16_sum(t[j], t[V / 4 + j]);
+  // lane bit 3 by the row mirror, bit 2 by the half-row mirror, bits 1 and 0
+  // by quad exchanges
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int j = 0; j < V / 8; ++j) {
+    const float keep = b3 ? t[V / 8 + j] : t[j], send = b3 ? t[j] : t[V / 8 + j];
+    t[j] = keep + q4_dpp<0x140>(send);
+  }
+  float sum;
+  if constexpr (LV == 3) {
+    sum = t[0] + q4_dpp<0x141>(t[0]);
+    sum += q4_dpp<0x4E>(sum);
+    sum += q4_dpp<0xB1>(sum);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V / 16; ++j) {
+      const float keep = b2 ? t[V / 16 + j] : t[j], send = b2 ? t[j] : t[V / 16 + j];
+      t[j] = keep + q4_dpp<0x141>(send);
+    }
+    if constexpr (LV == 4) {
+      sum = t[0] + q4_dpp<0x4E>(t[0]);
+    } else {
+      const float keep = b1 ? t[1] : t[0], send = b1 ? t[0] : t[1];
+      sum = keep + q4_dpp<0x4E>(send);
+    }
+    sum += q4_dpp<0xB1>(sum);
+  }
+  if ((lane & ((64 >> LV) - 1)) != 0) return;
+  const int idx = lane >> (6 - LV);
+  const int r = idx >> 2, m = idx & 3;
+  const int64_t n = n0 + r;
+  if (m >= M || n >= N) return;
+  const float bv = p.bias ? p.bias[n] : 0.0f;
+  p.y[m * N + n] = sm[m] * (sum * 0.0625f) + bv;
 }
 
 // ----------------------------------------------------------------- tiled
@@ -524,7 +696,18 @@ void launch_tiled(const Q4Args &a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
-  if (a.M <= kQ4StreamMaxM) {
+  if (a.M <= kQ4FewMaxM && a.K <= kQ4FewMaxK) {
+    // 4 waves of 2 channels; 1, 2 or 4 pieces of 1 KB per channel row
+    constexpr int W = 4, RW = 2;
+    const dim3 grid((unsigned)((a.N + W * RW - 1) / (W * RW)));
+    const size_t lds = (size_t)((a.M * a.K + 1023) / 1024 * 1024);
+    if (a.K <= 2048)
+      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 1>), grid, dim3(64 * W), lds, st, a);
+    else if (a.K <= 4096)
+      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 2>), grid, dim3(64 * W), lds, st, a);
+    else
+      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 4>), grid, dim3(64 * W), lds, st, a);
+  } else if (a.M <= kQ4StreamMaxM) {
     // 8-channel tiles for M <= 2, 16 otherwise; waves per workgroup (splitting
     // K) only while the wave-tiles are fewer than ~384: these waves are short
     // and few, and a K split adds a cross-wave reduction to each

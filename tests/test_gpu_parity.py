@@ -425,6 +425,39 @@ def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
     check_float(y, o["y"], o["tol"], FP32, f"dq8ca {wfmt} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (2, 17, 64), (3, 100, 2048), (4, 15, 2080),
+                                   (4, 1000, 4096), (1, 33, 4128), (4, 70, 8192), (3, 9, 8224),
+                                   (4, 11008, 4096)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_dq8ca_q4_few_rows(M, N, K, with_bias):
+    """M <= 4 and K <= 8192 run the few-rows 4-bit kernel (dot4 group sums on
+    1, 2 or 4 contiguous 1 KB pieces per channel row, the last partly past K;
+    N not a multiple of 8); K = 8224 takes the general streaming kernel. Rows:
+    all zero, one-sided positive, one-sided negative, a saturating outlier."""
+    say("dq8ca q4 small M", M, N, K, with_bias)
+    g = workloads.gen(660 + M + N + K)
+    x = workloads.small_matrix(g, M, K)
+    x[0] = 0.0 if M > 1 else x[0]
+    if M > 1:
+        x[1] = x[1].abs()
+    if M > 2:
+        x[2] = -x[2].abs()
+    if M > 3:
+        x[3, K // 2] = 3000.0
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    b = workloads.small_matrix(g, 1, N)[0] if with_bias else None
+    y, wq, wsc, xs, xz, group = _dq8ca_case(x, w, aql.AQL_W_Q4GSW, b)
+    o = oracle.linear_dq8ca(x.numpy(), wq, wsc, aql.AQL_W_Q4GSW, group, None if b is None else b.numpy())
+    assert np.array_equal(xs.view(np.uint32), o["x_scale"].view(np.uint32))
+    assert np.array_equal(xz, o["x_zp"])
+    check_float(y, o["y"], o["tol"], FP32, f"dq8ca q4 small {M}x{N}x{K}")
+    # without the qparams outputs
+    q4, gs, gsum = aql.aql_quantize_weight_q4gsw(dev(w), 32)
+    y2 = aql.aql_linear_dq8ca(dev(x), q4, gs, gsum, aql.AQL_W_Q4GSW, 32,
+                              None if b is None else dev(b))
+    assert np.array_equal(host(y2), y)
+
+
 @pytest.mark.parametrize("M,N,K", [(2000, 4100, 96), (1500, 4100, 160)])
 def test_dq8ca_q4_large_tiles_ragged(M, N, K):
     """Enough rows and columns for the 128 x 128 tiles (2000 x 4100) and the

@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="bound on the oracle's CPU time for cpu_baseline")
     ap.add_argument("--only", default=None,
-                    help="run just one workload (sweep|llm7b|q8ta|dq8ca|quant|calib|gptq|copy), or a "
+                    help="run just one workload (sweep|chain|llm7b|q8ta|dq8ca|quant|calib|gptq|copy), or a "
                          "measurement outside the default run (wsweep: working-set sweep; oracle: "
                          "the CPU oracle at full size beside the GPU)")
     ap.add_argument("--no-settle", action="store_true",
@@ -265,6 +265,63 @@ def sweep_as_graph(torch, aql, calls, step_bytes, reps=60):
            "frac_hbm": step_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS}
     say(row)
     return row
+
+
+def sec_decode_chain(torch, aql, workloads, dev, copies=3):
+    """Secondary row: the decode sweep with the dependencies of a real decode
+    step (flashrt schemes, W8A16Decode on a decoder_ffn seam). Per layer one
+    grouped launch computes up and gate from the same x, then down reads up's
+    output (the gated activation between them is not part of the quantized
+    linear and is left out: down reads the up projection as it is), and the
+    next layer reads down's output. 64 launches per step over the same 237 MB
+    of weights as the headline; 3 weight copies rotate. Timed eagerly and as
+    one HIP graph per copy."""
+    layers = workloads.smolvlm(seed=0)
+    F, H = workloads.SMOLVLM_FFN, workloads.SMOLVLM_HIDDEN
+    base = []
+    for L in layers:
+        e = {}
+        for wn in ("w_up", "w_gate", "w_down"):
+            q, s, _ = aql.aql_quantize_weight_int8(L[wn].to(dev), aql.AQL_WQ_SYM127)
+            e[wn] = (q, s)
+        base.append(e)
+    sets = [base] + [[{k: (v[0].clone(), v[1].clone()) for k, v in e.items()} for e in base]
+                     for _ in range(copies - 1)]
+    x0 = layers[0]["x_up"].to(dev)
+    acts = [(torch.empty(1, F, dtype=torch.bfloat16, device=dev),
+             torch.empty(1, F, dtype=torch.bfloat16, device=dev),
+             torch.empty(1, H, dtype=torch.bfloat16, device=dev)) for _ in layers]
+    steps = []
+    for c in range(copies):
+        st = []
+        for li, e in enumerate(sets[c]):
+            x = x0 if li == 0 else acts[li - 1][2]
+            yu, yg, yd = acts[li]
+            plan = aql.aql_w8a16_group_plan([(x, e["w_up"][0], e["w_up"][1], None, yu),
+                                             (x, e["w_gate"][0], e["w_gate"][1], None, yg)])
+            st.append((plan, yu, e["w_down"][0], e["w_down"][1], yd))
+        steps.append(st)
+    del layers
+
+    def step(i):
+        for plan, yu, qd, sd, yd in steps[i]:
+            aql.aql_linear_w8a16_grouped(*plan)
+            aql.aql_linear_w8a16(yu, qd, sd, None, yd)
+
+    step_bytes = 32 * (2 * (F * H + 4 * F + 2 * H + 2 * F) + (H * F + 4 * H + 2 * F + 2 * H))
+    for i in range(copies):
+        step(i)
+    eager, _ = event_time_ms(torch, step, 20, copies)
+    med, _ = event_time_ms(torch, step, 20, copies, graph=True)
+    rows = []
+    for how, ms in (("eager", eager), ("HIP graph", med)):
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        rows.append({"workload": f"smolvlm500m decode step with dependencies, {how}: 32 x (grouped "
+                                 f"up+gate sharing x, then down on up's output), 64 launches",
+                     "us": ms * 1e3, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                     "us_per_launch": ms * 1e3 / 64})
+        say(rows[-1])
+    return rows
 
 
 # -------------------------------------------------------------- secondary
@@ -727,6 +784,7 @@ def main():
     secondary = []
     if args.only is not None and args.only != "sweep":
         fn = {"llm7b": sec_llm7b, "q8ta": sec_q8ta, "dq8ca": sec_dq8ca, "quant": sec_quant,
+              "chain": sec_decode_chain,
               "calib": sec_calib, "copy": sec_copy, "gptq": sec_gptq, "wsweep": sec_wsweep,
               "oracle": sec_oracle}[args.only]
         print(json.dumps({"only": args.only, "rows": fn(torch, aql, workloads, dev)}), flush=True)
@@ -736,6 +794,9 @@ def main():
     if args.only is None and not args.no_secondary:
         secondary.append(sweep_as_graph(torch, aql, calls, step_bytes))
     del calls
+    torch.cuda.empty_cache()
+    if args.only is None and not args.no_secondary:
+        secondary += sec_decode_chain(torch, aql, workloads, dev)
     torch.cuda.empty_cache()
     if args.only is None and not args.no_secondary:
         for fn in (sec_llm7b, sec_q8ta, sec_dq8ca, sec_quant, sec_calib, sec_gptq):

@@ -251,3 +251,53 @@ def test_w8a16_grouped_paired_tiles_ragged_n():
     for (x, q, s, _, y), xc in zip(probs, refs):
         yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s), None)
         check_float(host(y.float()), yref, tol, BF16, f"paired ragged {tuple(y.shape)}")
+
+
+def test_w8a16_decode_step_with_dependencies():
+    """The dependent decode step the benchmark times: per layer one grouped
+    launch of up and gate on the same x, then down on up's output, the next
+    layer on down's output (8 layers, in a HIP graph replayed twice). Each
+    launch's output is checked against the oracle on the input that launch
+    actually read."""
+    layers = workloads.smolvlm(seed=2, layers=8)
+    F, H = workloads.SMOLVLM_FFN, workloads.SMOLVLM_HIDDEN
+    x0 = dev(layers[0]["x_up"])
+    acts, work = [], []
+    for li, L in enumerate(layers):
+        qs = {wn: aql.aql_quantize_weight_int8(dev(L[wn]), aql.AQL_WQ_SYM127)[:2]
+              for wn in ("w_up", "w_gate", "w_down")}
+        yu = torch.empty(1, F, dtype=torch.bfloat16, device=DEV)
+        yg = torch.empty(1, F, dtype=torch.bfloat16, device=DEV)
+        yd = torch.empty(1, H, dtype=torch.bfloat16, device=DEV)
+        x = x0 if li == 0 else acts[-1][2]
+        plan = aql.aql_w8a16_group_plan([(x, *qs["w_up"], None, yu), (x, *qs["w_gate"], None, yg)])
+        acts.append((yu, yg, yd))
+        work.append((x, plan, qs, yu, yg, yd))
+
+    def step():
+        for x, plan, qs, yu, yg, yd in work:
+            aql.aql_linear_w8a16_grouped(*plan)
+            aql.aql_linear_w8a16(yu, *qs["w_down"], None, yd)
+
+    def check(what):
+        for li, (x, plan, qs, yu, yg, yd) in enumerate(work):
+            xb = bits(x)
+            for y, wn, xin in ((yu, "w_up", xb), (yg, "w_gate", xb), (yd, "w_down", bits(yu))):
+                yref, tol = oracle.linear_w8a16(xin, host(qs[wn][0]), host(qs[wn][1]))
+                check_float(host(y.float()), yref, tol, BF16, f"{what} layer {li} {wn}")
+
+    step()
+    check("eager")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(2):
+        for yu, yg, yd in acts:
+            yu.fill_(float("nan"))
+            yg.fill_(float("nan"))
+            yd.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"graph replay {rep}")

@@ -265,13 +265,20 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_few(Q4Args p) {
     }
   }
   {
+    // LDS row m holds the first 16 code bytes of every group, then the second
+    // 16 (unit u = 16-byte slot: half h = u / G, group u % G), so a lane's two
+    // reads of its group are each contiguous across the wave (no bank conflicts)
     const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, (uint32_t)(M * K));
     const int nch = (int)((M * K + 1023) >> 10);
     const uint32_t base = (uint32_t)(uintptr_t)xl;
-    for (int c = wave; c < nch; c += W)
+    for (int c = wave; c < nch; c += W) {
+      const int u = 64 * c + lane, m = (int)(u / (2 * G)), rest = (int)(u % (2 * G));
+      const int h = (int)(rest / G), gg = (int)(rest % G);
+      const int src = m < M ? (int)((int64_t)m * K + 32LL * gg + 16 * h) : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + 1024u * c), 16,
-          (int)(16u * lane + 1024u * c), 0, 0, 0);
+          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + 1024u * c), 16, src, 0,
+          0, 0);
+    }
     if (wave == 0 && lane < 4) {
       qs_s[lane] = lane < M ? p.xs[lane] : 0.0f;
       qs_z[lane] = lane < M ? (float)p.xz[lane] : 0.0f;
@@ -299,9 +306,9 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_few(Q4Args p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // rows past M read row 0 (their sums are never written)
-      const int xo = (g < G ? (int)(32 * g) : 0) + (m < M ? m * (int)K : 0);
+      const int xo = (g < G ? (int)(16 * g) : 0) + (m < M ? m * (int)K : 0);
       xv[m][0] = *reinterpret_cast<const i32x4 *>(xl + xo);
-      xv[m][1] = *reinterpret_cast<const i32x4 *>(xl + xo + 16);
+      xv[m][1] = *reinterpret_cast<const i32x4 *>(xl + xo + 16 * (int)G);
     }
 #pragma unroll
     for (int r = 0; r < RW; ++r) {

@@ -20,6 +20,15 @@ constexpr int64_t kW8A16ContigMaxK = 8192;
 hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const float *scale,
                             const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st);
 
+// 2 <= M <= kW8A16FewMaxM rows over contiguous row pieces (bf16 dot2 on the
+// widened weights), used by launch_w8a16 for kW8A16FewMinK <= K <= kW8A16FewMaxK.
+constexpr int64_t kW8A16FewMaxM = 4;
+constexpr int64_t kW8A16FewMinK = 2048;
+constexpr int64_t kW8A16FewMaxK = 16384;
+hipError_t launch_w8a16_mfew(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                             const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
+                             hipStream_t st);
+
 // Launch shape of the W8A16 kernel: waves per channel group (they split K),
 // groups of 4 output channels per wave tile (1, 2 or 4) and blocks of 4 rows of
 // x per tile (1, 2 or 4; 0 selects the single-row tile, M = 1; kW8A16Skinny

@@ -657,6 +657,163 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_m1c(const uint16_t *__restrict
   y[n] = f32_to_bf16_rne(scale[n] * sum + bv);
 }
 
+// A few rows of x (2 <= M <= 4), contiguous form: the pieces and the wave
+// split of k_w8a16_m1c, with MR rows of x in registers as bf16 pairs and each
+// weight dword widened once (exact) and multiplied into the MR rows by
+// v_dot2_f32_bf16 (two products, fp32 accumulate). The R x MR lane partials
+// (R = 8 channels) go through the same kind of transposing butterfly.
+// a.lo * b.lo + a.hi * b.hi + c (bf16 pairs, fp32 accumulate), in the
+// three-operand VOP3P form: chains of the two-operand accumulate form that
+// the compiler picks for the builtin (v_dot2c_f32_bf16) gave wrong sums here.
+__device__ __forceinline__ float dot2_bf16(int a, int b, float c) {
+  float d;
+  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+template <int W, int P, int MR>
+__global__ __launch_bounds__(64 * W) void k_w8a16_mfew(const uint16_t *__restrict__ x, int64_t M,
+                                                        int64_t K, const int8_t *__restrict__ q,
+                                                        const float *__restrict__ scale,
+                                                        const uint16_t *__restrict__ bias,
+                                                        int64_t N, uint16_t *__restrict__ y) {
+  constexpr int R = 8;           // channels per workgroup
+  constexpr int NL = R * P;      // weight loads per wave
+  constexpr int B = 4;           // loads per batch
+  constexpr int NB = (NL + B - 1) / B;
+  constexpr int V = R * MR;      // partial sums per lane
+  static_assert(V == 16 || V == 32, "MR in {2, 4}");
+  __shared__ float red[W][V];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = (int64_t)blockIdx.x * R;
+  const int64_t nrows = N - n0 < R ? N - n0 : R;
+  const int64_t kw = ((K + W - 1) / W + 15) / 16 * 16;
+  const int64_t k0 = wave * kw;
+  const int64_t k1 = K < k0 + kw ? K : k0 + kw;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(q + n0 * K, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (uint32_t)(2 * K * M));
+
+  int kk[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int64_t k = k0 + 1024 * p + 16 * lane;
+    kk[p] = k < k1 ? (int)k : -1;
+  }
+  auto issue = [&](int b, i32x4 *dst) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int L = b * B + u;
+      if (L < NL) {
+        const int r = L % R, p = L / R;
+        const int off = kk[p] >= 0 ? (int)((uint32_t)r * (uint32_t)K + (uint32_t)kk[p]) : OOB;
+        dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 2);
+      }
+    }
+  };
+
+  i32x4 wb0[B], wb1[B];
+  issue(0, wb0);
+  i32x4 xr[P][MR][2];  // bf16 pairs: 16 values per lane, piece and row (rows past M: zero)
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const bool in = kk[p] >= 0 && m < M;
+      const int off = in ? 2 * (m * (int)K + kk[p]) : OOB;
+      xr[p][m][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      xr[p][m][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? off + 16 : OOB, 0, 0);
+    }
+  if (NB > 1) issue(1, wb1);
+
+  float acc[R][MR];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[r][m] = 0.0f;
+  auto consume = [&](int b, const i32x4 *src) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int L = b * B + u;
+      if (L < NL) {
+        const int r = L % R, p = L / R;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // weights k = 4e .. 4e + 3 of the lane's 16, as two bf16 pairs
+          const i32x2 w2 = __builtin_bit_cast(i32x2, widen4(src[u][e]));
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            const i32x4 xv = xr[p][m][e >> 1];
+            const int xa = xv[2 * (e & 1)], xb = xv[2 * (e & 1) + 1];
+            acc[r][m] = dot2_bf16(xa, w2[0], acc[r][m]);
+            acc[r][m] = dot2_bf16(xb, w2[1], acc[r][m]);
+          }
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    __builtin_amdgcn_sched_barrier(0);
+    consume(b, (b & 1) ? wb1 : wb0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (b + 2 < NB) issue(b + 2, (b & 1) ? wb1 : wb0);
+  }
+
+  // transposing butterfly over lane bits 5, 4, 3, 2 (and 1 for V = 32), then
+  // plain sums; lane l ends with value index l >> (6 - log2 V)
+  constexpr int LV = V == 16 ? 4 : 5;
+  float t[V];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) t[MR * r + m] = acc[r][m];
+#pragma unroll
+  for (int j = 0; j < V / 2; ++j) t[j] = swap32_sum(t[j], t[V / 2 + j]);
+#pragma unroll
+  for (int j = 0; j < V / 4; ++j) t[j] = swap16_sum(t[j], t[V / 4 + j]);
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int j = 0; j < V / 8; ++j) {
+    const float keep = b3 ? t[V / 8 + j] : t[j], send = b3 ? t[j] : t[V / 8 + j];
+    t[j] = keep + dpp_f32<kDppRowMirror>(send);
+  }
+#pragma unroll
+  for (int j = 0; j < V / 16; ++j) {
+    const float keep = b2 ? t[V / 16 + j] : t[j], send = b2 ? t[j] : t[V / 16 + j];
+    t[j] = keep + dpp_f32<kDppRowHalfMirror>(send);
+  }
+  float sum;
+  if constexpr (LV == 4) {
+    sum = t[0] + dpp_f32<kDppQuadXor2>(t[0]);
+  } else {
+    const float keep = b1 ? t[1] : t[0], send = b1 ? t[0] : t[1];
+    sum = keep + dpp_f32<kDppQuadXor2>(send);
+  }
+  sum += dpp_f32<kDppQuadXor1>(sum);
+  const int idx = lane >> (6 - LV);  // = MR r + m
+  const bool lead = (lane & ((64 >> LV) - 1)) == 0;
+  if constexpr (W > 1) {
+    if (lead) red[wave][idx] = sum;
+    __syncthreads();
+    if (wave != 0 || lane >= V) return;
+    sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][lane];
+    const int r = lane / MR, m = lane % MR;
+    const int64_t n = n0 + r;
+    if (m >= M || n >= N) return;
+    const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+    y[m * N + n] = f32_to_bf16_rne(scale[n] * sum + bv);
+  } else {
+    if (!lead) return;
+    const int r = idx / MR, m = idx % MR;
+    const int64_t n = n0 + r;
+    if (m >= M || n >= N) return;
+    const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+    y[m * N + n] = f32_to_bf16_rne(scale[n] * sum + bv);
+  }
+}
+
 constexpr int M1_TG = 2;  // single-row tile: 8 channels per wave tile
 constexpr int M1_U = 2;   // steps per fetched batch
 
@@ -938,11 +1095,35 @@ hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const
   return hipGetLastError();
 }
 
+hipError_t launch_w8a16_mfew(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                             const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
+                             hipStream_t st) {
+  if (M < 2 || M > kW8A16FewMaxM || K < kW8A16FewMinK || K > kW8A16FewMaxK || K % 16)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + 7) / 8));
+  auto go = [&](auto kern, int W) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * W), 0, st, x, M, K, q, scale, bias, N, y);
+  };
+  // waves split K so that each keeps one or two pieces of 1 KB per row
+  if (M == 2) {
+    if (K <= 4096) go(k_w8a16_mfew<4, 1, 2>, 4);
+    else if (K <= 8192) go(k_w8a16_mfew<4, 2, 2>, 4);
+    else go(k_w8a16_mfew<8, 2, 2>, 8);
+  } else {
+    if (K <= 4096) go(k_w8a16_mfew<4, 1, 4>, 4);
+    else if (K <= 8192) go(k_w8a16_mfew<4, 2, 4>, 4);
+    else go(k_w8a16_mfew<8, 2, 4>, 8);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                         hipStream_t st) {
   if (M == 1 && K >= kW8A16ContigMinK && K <= kW8A16ContigMaxK)
     return launch_w8a16_m1c(x, K, q, scale, bias, N, y, st);
+  if (M >= 2 && M <= kW8A16FewMaxM && K >= kW8A16FewMinK && K <= kW8A16FewMaxK)
+    return launch_w8a16_mfew(x, M, K, q, scale, bias, N, y, st);
   return launch_w8a16_shape(w8a16_shape(M, N, K), x, M, K, q, scale, bias, N, y, st);
 }
 

@@ -383,6 +383,9 @@ def sec_q8ta(torch, aql, workloads, dev):
                                                  two, s2, 0, y, wsb)
         for i in range(ncopy):
             fn(i)
+        fn = raw_call(aql, torch, "aql_linear_q8ta_q8csw",
+                      [(x, M, K, s1, z1, int(two), s2, 0, qs[i][0], qs[i][2], qs[i][1], None, N,
+                        y, wsb, wsb.numel()) for i in range(ncopy)])
         med, _ = event_time_ms(torch, fn, 40, ncopy, warm_ms=40.0)
         pro = lambda i: aql.aql_quantize_act_per_tensor(x, s1, z1, two, s2, 0, xq1, xq2)
         pmed, _ = event_time_ms(torch, pro, 40, 1, graph=True)

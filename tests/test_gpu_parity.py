@@ -226,12 +226,15 @@ def test_w8a16_tiny():
                                    (1, 4100, 48), (1, 70001, 32), (1, 1000, 8208),
                                    (1, 4100, 12288), (1, 9, 2048), (1, 8, 4096), (1, 17, 2064),
                                    (1, 3, 8192), (1, 5, 6160), (1, 13, 65536),
-                                   (1, 2049, 4080)])
+                                   (1, 2049, 4080), (2, 9, 2048), (4, 17, 16384), (3, 1000, 6160),
+                                   (4, 8, 4096), (2, 4100, 14336), (3, 7, 16400)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_shapes(M, N, K, with_bias):
     """Ragged W8A16 shapes for every M band. M = 1 with 2048 <= K <= 8192 runs
-    the contiguous single-row kernel (one or two pieces of 1 KB per wave and
-    row, the last piece partly past K, N not a multiple of 8)."""
+    the contiguous single-row kernel, 2 <= M <= 4 with 2048 <= K <= 16384 the
+    contiguous few-rows kernel (one or two pieces of 1 KB per wave and row,
+    the last piece partly past K, N not a multiple of 8); K = 16400 at M = 3
+    falls back to the skinny tile."""
     say("w8a16", M, N, K, with_bias)
     g = workloads.gen(400 + M + N + K)
     w = workloads.small_matrix(g, N, K, std=0.02)

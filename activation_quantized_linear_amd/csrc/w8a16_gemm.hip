@@ -7,17 +7,24 @@
 //
 // Tiles: on large grids 128 rows of x x 256 output channels per workgroup of 8
 // waves side by side along N (k_w8a16_gemm_wide, below); otherwise BM (64 or
-// 128) rows x 128 channels, waves (BM / 64) x 2 quadrants of 64 x 64 (4 x 4
-// MFMA tiles each) times 2 halves of every 64-k stage, the halves' fp32
-// accumulators added once at the end.
+// 128) rows x 128 channels (k_w8a16_gemm): a group of waves covers the tile
+// for one 64-k stage, (BM / 64) x 2 quadrants of 64 x 64 (4 x 4 MFMA tiles
+// each) times 2 halves of the stage, and for the 64-row tile two such groups
+// take alternate stages, which puts two waves on every SIMD (one wave's
+// widening then overlaps the other's MFMAs). The partial fp32 accumulators
+// are added once at the end.
 // Operands go global -> LDS by buffer loads that write LDS directly (hardware
 // zero-fill past M, N and K): x as bf16 rows of 128 B, the weights as int8 rows
 // of 64 B (half the bytes of bf16; they are widened after the fragment read).
-// A 4-stage ring (2 stages for the wide tile on the largest grids) keeps the
-// next stages in flight behind exact vmcnt waits and a fence-free barrier (a
-// straight-line loop, so the compiler's wait counts stay exact). x rows store their 16-byte chunks XOR-swizzled by (row / 2) mod 8 and
-// weight rows by (row / 4) mod 4, which makes every fragment read conflict-free.
+// A ring of stages (4 or 8; 2 for the wide tile on the largest grids) keeps
+// the next stages in flight behind exact vmcnt waits and a fence-free barrier
+// (a straight-line loop, so the compiler's wait counts stay exact); when K is
+// a multiple of 64 the k advance of a load is a scalar offset. x rows store
+// their 16-byte chunks XOR-swizzled by (row / 2) mod 8 and weight rows by
+// (row / 4) mod 4, which makes every fragment read conflict-free.
 // The output tile is staged in LDS as bf16 and written as whole rows.
+#include <type_traits>
+
 #include "common.h"
 #include "w8a16_gemm.h"
 
@@ -27,7 +34,7 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BN = 128, BK = 64, STAGES = 4;
+constexpr int BN = 128, BK = 64;
 constexpr int OOB = 0x40000000;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
@@ -51,32 +58,60 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n (0..63: bits 3:0 and 15:14)
+// and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 __device__ __forceinline__ int swz_x(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz_w(int row) { return (row >> 2) & 3; }
 
-template <int WM>
+// BM = 64 WM rows. A group of waves covers the tile for one 64-k stage: every
+// wave of it computes 16 TI rows x 64 channels over one 32-k half of the stage,
+// so a group has NG = (BM / 16 TI) x 2 x 2 waves. KP groups take consecutive
+// stages (stage KP t + kp in step t), which puts KP waves on every SIMD to
+// overlap one wave's weight widening with another's MFMAs; SG stages of LDS
+// form the ring (SG / KP steps). The partial sums of the 2 KP waves that share
+// an output block are added through LDS at the end.
+template <int WM, int TI, int SG, int KP>
 struct GemmLds {
   static constexpr int BM = 64 * WM;
+  static constexpr int WMW = BM / (16 * TI);    // waves along M
+  static constexpr int NG = 4 * WMW;            // waves per group
+  static constexpr int NW = KP * NG;            // waves per workgroup
+  static constexpr int PS = SG / KP;            // steps in the ring
+  static constexpr int NXL = (BM / 8) / NG;     // x loads per wave per step
+  static constexpr int NWL = 8 / NG;            // weight loads per wave per step
   static constexpr int XS = BM * 128;           // x stage: BM rows x 64 bf16
   static constexpr int WS = BN * 64;            // weight stage: 128 rows x 64 int8
   static constexpr int STAGE = XS + WS;
-  static constexpr int RING = STAGES * STAGE;
-  static constexpr int XCH = 2 * WM * 16 * 64 * 16;  // fp32 half-sums of the kh = 1 waves
+  static constexpr int RING = SG * STAGE;
+  static constexpr int XCH = (NW - 2 * WMW) * TI * 4 * 64 * 16;  // partial sums to add
   static constexpr int TLD = BN + 8;            // bf16 per staged output row
   static constexpr int TILE = BM * TLD * 2;
   static constexpr int BYTES = RING > XCH + TILE ? RING : XCH + TILE;
+  static_assert(NXL * NG == BM / 8 && NWL * NG == 8, "load slots split evenly");
+  static_assert(SG % KP == 0 && PS >= 3, "ring of whole steps, one read ahead");
 };
 
-template <int WM>
-__global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restrict__ x,
-                                                          const int8_t *__restrict__ q,
-                                                          const float *__restrict__ scale,
-                                                          const uint16_t *__restrict__ bias,
-                                                          uint16_t *__restrict__ y, int64_t M,
-                                                          int64_t N, int64_t K, int tiles_m,
-                                                          int tiles_n) {
-  using L = GemmLds<WM>;
-  constexpr int BM = L::BM, NW = 4 * WM, NL = WM == 1 ? 4 : 3;  // loads per wave per stage
+// RAG: K is not a multiple of 64, so the last stage is partial and every load
+// checks its chunk against the row end; otherwise the k advance of a load is a
+// uniform (scalar) offset and costs no vector instruction.
+template <int WM, int TI, int SG, int KP, bool RAG>
+__global__ __launch_bounds__((64 * GemmLds<WM, TI, SG, KP>::NW)) void k_w8a16_gemm(
+    const uint16_t *__restrict__ x, const int8_t *__restrict__ q, const float *__restrict__ scale,
+    const uint16_t *__restrict__ bias, uint16_t *__restrict__ y, int64_t M, int64_t N, int64_t K,
+    int tiles_m, int tiles_n) {
+  using L = GemmLds<WM, TI, SG, KP>;
+  constexpr int BM = L::BM, NG = L::NG, NW = L::NW, PS = L::PS, NXL = L::NXL;
+  constexpr int NL = L::NXL + L::NWL;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int nt = tiles_m * tiles_n;
@@ -88,29 +123,31 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave / (2 * WM), wm = (wave >> 1) % WM, wn = wave & 1;
+  const int kp = wave / NG, wig = wave % NG;  // group, wave in group
+  const int kh = wig / (2 * L::WMW), wm = (wig >> 1) % L::WMW, wn = wig & 1;
   const int r = lane & 15, g = lane >> 4;
   const int64_t mval = M - m0 < BM ? M - m0 : BM;
   const int64_t nval = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, (uint32_t)(mval * K * 2));
   const __amdgpu_buffer_rsrc_t rq = rsrc(q + n0 * K, (uint32_t)(nval * K));
 
-  // Loads per stage: BM/8 x-slots (8 rows x 128 B) and 8 weight slots (16 rows
-  // x 64 B), NL per wave; load q of every wave is of one kind: q < 2 x-slot
-  // q * NW + wave, else weight slot (q - 2) * NW + wave.
+  // Each group loads the stages it computes. Loads per stage: BM/8 x-slots
+  // (8 rows x 128 B) and 8 weight slots (16 rows x 64 B), NL per wave of the
+  // group; load qq of every wave is of one kind: qq < NXL x-slot qq NG + wig,
+  // else weight slot (qq - NXL) NG + wig.
   uint32_t off[NL], ldso[NL], kstep[NL];
   int kin_lim[NL];
 #pragma unroll
   for (int qq = 0; qq < NL; ++qq) {
-    if (qq < 2) {
-      const int slot = qq * NW + wave;
+    if (qq < NXL) {
+      const int slot = qq * NG + wig;
       const int row = 8 * slot + (lane >> 3), c = (lane & 7) ^ swz_x(row);
       off[qq] = (uint32_t)row * (uint32_t)(2 * K) + 16u * c;
       ldso[qq] = (uint32_t)(slot * 1024);
       kstep[qq] = 128;
       kin_lim[qq] = (int)((2 * K - 16 * c + 127) / 128);
     } else {
-      const int slot = (qq - 2) * NW + wave;
+      const int slot = (qq - NXL) * NG + wig;
       const int row = 16 * slot + (lane >> 2), c = (lane & 3) ^ swz_w(row);
       off[qq] = (uint32_t)row * (uint32_t)K + 16u * c;
       ldso[qq] = (uint32_t)(L::XS + slot * 1024);
@@ -118,97 +155,153 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
       kin_lim[qq] = (int)((K - 16 * c + 63) / 64);
     }
   }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int kt) {
+  const int nk = (int)((K + BK - 1) / BK);  // stages
+  const uint32_t lds_base = (uint32_t)(uintptr_t)smem + (uint32_t)(kp * L::STAGE);
+  // this group's stage of step t into ring slot `slot`; a stage past K loads
+  // zeros (RAG) or stage 0 again, and its sums are skipped
+  auto issue = [&](int t, int slot) {
+    const int kt = KP * t + kp;
 #pragma unroll
     for (int qq = 0; qq < NL; ++qq) {
-      const uint32_t dst = lds_base + (uint32_t)((kt % STAGES) * L::STAGE) + ldso[qq];
-      const int o = kt < kin_lim[qq] ? (int)(off[qq] + kstep[qq] * (uint32_t)kt) : OOB;
+      const uint32_t dst = lds_base + (uint32_t)(slot * KP * L::STAGE) + ldso[qq];
+      int vo, so;
+      if constexpr (RAG) {
+        vo = kt < kin_lim[qq] ? (int)(off[qq] + kstep[qq] * (uint32_t)kt) : OOB;
+        so = 0;
+      } else {
+        vo = (int)off[qq];
+        so = kt < nk ? kt * (qq < NXL ? 128 : 64) : 0;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qq < 2 ? rx : rq, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16, o, 0,
-          0, 0);
+          qq < NXL ? rx : rq, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16, vo,
+          so, 0, 0);
     }
   };
 
   // fragment offsets within a stage
-  int fxo[4], fwo[4];
+  int fxo[TI], fwo[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int R = wm * 64 + i * 16 + r;
-    fxo[i] = R * 128 + 16 * ((4 * kh + g) ^ swz_x(R));
-    const int S = wn * 64 + i * 16 + r;
-    fwo[i] = L::XS + S * 64 + 16 * ((2 * kh + (g >> 1)) ^ swz_w(S)) + 8 * (g & 1);
+  for (int i = 0; i < TI; ++i) {
+    const int R = wm * 16 * TI + i * 16 + r;
+    fxo[i] = kp * L::STAGE + R * 128 + 16 * ((4 * kh + g) ^ swz_x(R));
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int S = wn * 64 + j * 16 + r;
+    fwo[j] = kp * L::STAGE + L::XS + S * 64 + 16 * ((2 * kh + (g >> 1)) ^ swz_w(S)) + 8 * (g & 1);
   }
 
-  f32x4 acc[4][4];
+  f32x4 acc[TI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int kt) {
-    const char *st = smem + (kt % STAGES) * L::STAGE;
-    bf16x8 fa[4], fb[4];
+  // Software pipeline, one step deep: step t reads stage t + 1's fragments
+  // from LDS and widens its weights between the MFMAs of stage t (whose
+  // operands were made ready in step t - 1), so the VALU work of the widening
+  // issues while the matrix core runs.
+  struct Frag {
+    bf16x8 a[TI];
+    bf16x8 b[4];
+  };
+  i32x2 wr[4];
+  auto read = [&](int slot, Frag &f) {
+    const char *st = smem + slot * KP * L::STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = *reinterpret_cast<const bf16x8 *>(st + fxo[i]);
-      const i32x2 w = *reinterpret_cast<const i32x2 *>(st + fwo[i]);
-      fb[i] = widen8((uint32_t)w[0], (uint32_t)w[1]);
-    }
-    __builtin_amdgcn_s_setprio(1);  // as in the wide tile below
+    for (int i = 0; i < TI; ++i) f.a[i] = *reinterpret_cast<const bf16x8 *>(st + fxo[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) wr[j] = *reinterpret_cast<const i32x2 *>(st + fwo[j]);
+  };
+  auto widen = [&](Frag &f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = widen8((uint32_t)wr[j][0], (uint32_t)wr[j][1]);
+  };
+  auto mma = [&](const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // interleave: the fragment reads first, then one MFMA per 3 VALU ops
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, TI + 4, 0);  // DS reads
+#pragma unroll
+    for (int u = 0; u < 4 * TI; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    }
   };
 
-  const int nk = (int)((K + BK - 1) / BK);
+  // steps of KP stages (a stage past K loads zeros and adds nothing)
+  const int ns = (int)((K + KP * BK - 1) / (KP * BK));
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
-  int kt = 0;
-  auto step = [&](int k) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-    __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
-    issue(k + STAGES - 1);
-    compute(k);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // this stage's fragment reads done
+  for (int t = 0; t < PS - 1; ++t) issue(t, t);
+  Frag cur, nxt;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (PS - 2)));
+  __builtin_amdgcn_s_barrier();  // step 0 complete everywhere
+  read(0, cur);
+  widen(cur);
+  int ts = 0;
+  // Step t: stage t + 1 must have landed (the loads of steps up to t + PS - 2
+  // are out, so at most NL (PS - 3) of this wave's may stay outstanding), and
+  // the slot refilled is that of step t - 1, whose fragments every wave has
+  // consumed before this barrier. u = t mod PS.
+  auto step = [&](int t, int u) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (PS - 3)));
+    __builtin_amdgcn_s_barrier();
+    issue(t + PS - 1, (u + PS - 1) % PS);
+    read((u + 1) % PS, nxt);
+    mma(cur);
+    widen(nxt);
+    interleave();
+    cur = nxt;
   };
-  // whole turns of the ring first: each stage's LDS offsets become constants
-  const int nmain = nk - (STAGES - 1);
-  for (; kt + STAGES - 1 < nmain; kt += STAGES) {
-#pragma unroll
-    for (int u = 0; u < STAGES; ++u) step(kt + u);
-  }
-  for (; kt < nmain; ++kt) step(kt);
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t) {
-    if (kt < nk) {
-      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 3)));
-      else __builtin_amdgcn_s_waitcnt(0x0F70);
-      __builtin_amdgcn_s_barrier();
-      compute(kt);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
+  // whole turns of the ring first: each step's LDS offsets become constants
+  const int nmain = ns - (PS - 1);
+  for (; ts + PS - 1 < nmain; ts += PS)
+    static_for<0, PS>([&](auto u) { step(ts + decltype(u)::value, decltype(u)::value); });
+  for (; ts < nmain; ++ts) step(ts, ts % PS);
+  // the last PS - 1 steps: nothing more is issued; the last loads were those
+  // of step ns - 1, so stage ts + 1 has landed with at most NL (ns - 2 - ts)
+  // of this wave's loads outstanding
+  static_for<0, PS - 1>([&](auto u) {
+    constexpr int left = PS - 3 - decltype(u)::value;
+    if (ts < ns) {
+      if (ts + 1 < ns) {  // (only the last step can hold a stage past K)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (left > 0 ? left : 0)));
+        __builtin_amdgcn_s_barrier();
+        read((ts + 1) % PS, nxt);
+        mma(cur);
+        widen(nxt);
+        interleave();
+      } else if (KP * ts + kp < nk) {
+        mma(cur);
+      }
+      cur = nxt;
     }
-    ++kt;
-  }
+    ++ts;
+  });
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  // ---- add the K halves, then scale + bias + bf16 into the LDS output tile.
-  // acc[i][j] lane holds D[4g + v][r] of MFMA tile (i, j): row m, column n.
+  // ---- add the partial sums, then scale + bias + bf16 into the LDS output
+  // tile. acc[i][j] lane holds D[4g + v][r] of MFMA tile (i, j): row m, column
+  // n. Partner p = 2 kp + kh (1 .. 2 KP - 1) of output block b = 2 wm + wn
+  // writes slot (p - 1) 2 WMW + b; partner 0 adds them in the order of p.
   f32x4 *xch = reinterpret_cast<f32x4 *>(smem);
-  if (kh == 1) {
+  const int part = 2 * kp + kh, blk = 2 * wm + wn;
+  if (part != 0) {
+    const int slot = (part - 1) * 2 * L::WMW + blk;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xch[((wave - 2 * WM) * 16 + i * 4 + j) * 64 + lane] = acc[i][j];
+      for (int j = 0; j < 4; ++j) xch[(slot * 4 * TI + i * 4 + j) * 64 + lane] = acc[i][j];
   }
   __syncthreads();
   uint16_t *tl = reinterpret_cast<uint16_t *>(smem + L::XCH);
-  if (kh == 0) {
+  if (part == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = wn * 64 + j * 16 + r;
@@ -216,18 +309,21 @@ __global__ __launch_bounds__(256 * WM) void k_w8a16_gemm(const uint16_t *__restr
       const float s = n < N ? scale[n] : 0.0f;
       const float b = (n < N && bias) ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v4 = acc[i][j] + xch[(wave * 16 + i * 4 + j) * 64 + lane];
+      for (int i = 0; i < TI; ++i) {
+        f32x4 v4 = acc[i][j];
+#pragma unroll
+        for (int pp = 1; pp < 2 * KP; ++pp)
+          v4 += xch[(((pp - 1) * 2 * L::WMW + blk) * 4 * TI + i * 4 + j) * 64 + lane];
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          tl[(wm * 64 + i * 16 + 4 * g + v) * L::TLD + col] = f32_to_bf16_rne(s * v4[v] + b);
+          tl[(wm * 16 * TI + i * 16 + 4 * g + v) * L::TLD + col] = f32_to_bf16_rne(s * v4[v] + b);
       }
     }
   }
   __syncthreads();
   // 16 lanes x 16 B per 256-byte row
   const bool vec = (N & 7) == 0;
-  for (int u = tid; u < BM * 16; u += 256 * WM) {
+  for (int u = tid; u < BM * 16; u += 64 * NW) {
     const int row = u >> 4, c = u & 15;
     const int64_t m = m0 + row, n = n0 + 8 * c;
     if (m >= M || n >= N) continue;
@@ -465,28 +561,38 @@ hipError_t launch_wide(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
   return hipGetLastError();
 }
 
-template <int WM>
-hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
+template <int WM, int TI, int SG, int KP, bool RAG>
+hipError_t launch_wm_k(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
                      const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
-  using L = GemmLds<WM>;
+  using L = GemmLds<WM, TI, SG, KP>;
   static bool attr_set = false;
   if (!attr_set) {  // more than 64 KB of dynamic LDS; a launch the limit refuses reports itself
-    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm<WM>,
+    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm<WM, TI, SG, KP, RAG>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     (void)hipGetLastError();
     attr_set = true;
   }
   const int tiles_m = (int)((M + L::BM - 1) / L::BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(k_w8a16_gemm<WM>, dim3((unsigned)(tiles_m * tiles_n)), dim3(256 * WM),
-                     L::BYTES, st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL((k_w8a16_gemm<WM, TI, SG, KP, RAG>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(64 * L::NW), L::BYTES, st, x, q, scale, bias, y, M, N, K, tiles_m,
+                     tiles_n);
   return hipGetLastError();
+}
+
+template <int WM, int TI, int SG, int KP>
+hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
+                     const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
+  if (K % BK == 0) return launch_wm_k<WM, TI, SG, KP, false>(x, M, K, q, scale, bias, N, y, st);
+  return launch_wm_k<WM, TI, SG, KP, true>(x, M, K, q, scale, bias, N, y, st);
 }
 
 }  // namespace
 
 // 128 x 256 tiles from 160 of them on (fewer than one per CU still beats the
 // smaller tiles' extra round), two workgroups a CU from 512 on; else 128 x 128
-// tiles when those fill the CUs, else 64 x 128 tiles.
+// tiles when those fill the CUs, else 64 x 128 tiles with two stage groups
+// and an 8-stage ring (measured at M = 512, K = 14336, N = 4096: 74 us against
+// 95 us for one group of 4 waves).
 hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
                              hipStream_t st) {
@@ -494,8 +600,8 @@ hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8
   if (twide >= 512) return launch_wide<2>(x, M, K, q, scale, bias, N, y, st);
   if (twide >= 160) return launch_wide<4>(x, M, K, q, scale, bias, N, y, st);
   const int64_t t128 = ((M + 127) / 128) * ((N + BN - 1) / BN);
-  if (t128 >= 256) return launch_wm<2>(x, M, K, q, scale, bias, N, y, st);
-  return launch_wm<1>(x, M, K, q, scale, bias, N, y, st);
+  if (t128 >= 256) return launch_wm<2, 4, 4, 1>(x, M, K, q, scale, bias, N, y, st);
+  return launch_wm<1, 4, 8, 2>(x, M, K, q, scale, bias, N, y, st);
 }
 
 }  // namespace aql

@@ -728,10 +728,11 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
-    // 128 x 128 tiles once they give every CU a few; else 64 x 64 tiles with
-    // the groups split over two waves
+    // 128 x 128 tiles once there are more of them than CUs; else 64 x 64 tiles
+    // with the groups split over two waves (K = 4096, N = 11008: 93 vs 100 us
+    // at M = 512, 344 such tiles; 79 vs 35 us at M = 128)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
-    if (tl >= 512) launch_tiled<QTL>(a, st);
+    if (tl >= 320) launch_tiled<QTL>(a, st);
     else launch_tiled<QTS>(a, st);
   }
   return hipGetLastError();

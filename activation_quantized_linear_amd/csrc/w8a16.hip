@@ -1087,9 +1087,12 @@ hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const
                             const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
   if (K < kW8A16ContigMinK || K > kW8A16ContigMaxK || K % 16) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + 7) / 8));
-  // 4 waves split K, each with one or two pieces of 1 KB per row
+  // 4 waves split K, each with one or two pieces of 1 KB per row; one piece
+  // per row is consumed in batches of 2 loads (K = 4096, N = 14336: 10.66 us
+  // against 10.81 with batches of 4; a single launch of the read-only probe
+  // over the same 58.7 MB takes 10.39 us)
   if (K <= 4096)
-    hipLaunchKernelGGL((k_w8a16_m1c<4, 1>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
+    hipLaunchKernelGGL((k_w8a16_m1c<4, 1, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
   else
     hipLaunchKernelGGL((k_w8a16_m1c<4, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
   return hipGetLastError();

@@ -443,13 +443,15 @@ __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
 
 // 8 nibbles of one lane (k = 0..7 of its 8-k slice, k even in the low nibble
 // of each byte) -> bf16 136 + c in the order k = 0,4,1,5,2,6,3,7: dword i holds
-// nibbles i and i + 4, which one shift and one mask-or pull out together.
+// nibbles i and i + 4, which one shift and one mask-xor pull out together.
+// Flipping bit 3 of a two's-complement nibble adds 8 (mod 16), so c + 8 comes
+// from the same xor that sets the high byte 0x43: (raw & 0xF) ^ 0x4308 =
+// 0x4300 | (c + 8), the bf16 128 + (c + 8).
 __device__ __forceinline__ bf16x8 nib_bf16x8(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = ((u >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
+  for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) ^ 0x43084308u;
   return __builtin_bit_cast(bf16x8, r);
 }
 
@@ -552,15 +554,44 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
 #pragma unroll
         for (int i = 0; i < TI; ++i)
           corr[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bneg, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        // Row by row: the FMAs that fold row i - 1's group sums into f go
+        // between row i's MFMAs (whose results they do not need), so the
+        // vector ALU and the matrix core work side by side.
+        f32x4 tp[TJ], tc[TJ];
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+        for (int i = 0; i < TI; ++i) {
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], corr[i], 0, 0, 0);
+          for (int j = 0; j < TJ; ++j)
+            tc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], corr[i], 0, 0, 0);
+          if (i > 0) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) f[i][j][v] = __builtin_fmaf(gsv[j], t[v], f[i][j][v]);
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) f[i - 1][j][v] = __builtin_fmaf(gsv[j], tp[j][v], f[i - 1][j][v]);
           }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) tp[j] = tc[j];
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) f[TI - 1][j][v] = __builtin_fmaf(gsv[j], tp[j][v], f[TI - 1][j][v]);
         __builtin_amdgcn_s_setprio(0);
+        // issue order: the fragment reads, the corrections with the unpacking
+        // between them, then per row its MFMAs each followed by 4 of the
+        // previous row's FMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, TI + 2 * TJ, 0);
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (9 * TJ + TI - 1) / TI, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, TJ, 0);
+#pragma unroll
+        for (int u = 0; u < (TI - 1) * TJ; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       }
     }
   };

@@ -113,7 +113,8 @@ struct GroupHeader {
   int32_t tgroups;       // 4-channel groups per tile
   int32_t cgroups;       // wave tiles per workgroup along N (single-row tile)
   int32_t xlds;          // LDS bytes holding x (single-row tile; 0: none)
-  int32_t reserved[7];
+  int32_t kind;          // 0: the tile kernels above; 1: single-row pieces kernel
+  int32_t reserved[6];
 };
 static_assert(sizeof(GroupHeader) == 64, "table header");
 constexpr uint32_t kGroupMagic = 0x47514c41u;  // "ALQG"
@@ -338,6 +339,8 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
   GroupHeader *h = static_cast<GroupHeader *>(table);
   aql::W8A16GroupEntry *e = reinterpret_cast<aql::W8A16GroupEntry *>(h + 1);
   // One launch shape for the whole group, from the smallest K and the largest M.
+  // Groups of single-row problems with kW8A16PiecesMinK <= K <= kW8A16PiecesMaxK
+  // take the pieces kernel (whole 1 KB row pieces, no bytes read past a row).
   int64_t kmin = 0, kmax = 0, mmax = 0, nsum = 0;
   for (int i = 0; i < count; ++i) {
     const aql_w8a16_problem &p = problems[i];
@@ -350,16 +353,24 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
     mmax = p.M > mmax ? p.M : mmax;
     nsum += p.N * ((p.M + 15) / 16);
   }
+  const bool pieces = mmax == 1 && kmin >= aql::kW8A16PiecesMinK && kmax <= aql::kW8A16PiecesMaxK;
   aql::W8A16Shape sh = aql::w8a16_shape(mmax ? mmax : 1, nsum ? nsum : 1, kmin ? kmin : 16);
   if (sh.waves > 8) sh.waves = 8;
   // x shared through LDS only if every problem's x fits
   if (sh.mblocks == 0) sh.xlds = aql::w8a16_xlds_bytes(kmax ? kmax : 16);
-  const int64_t rows = 4 * sh.tgroups * sh.cgroups;
+  if (pieces) {
+    sh = aql::W8A16Shape{};
+    sh.waves = 4;
+    sh.tgroups = 2;
+    sh.mblocks = 0;
+  }
   int64_t blocks = 0;
   int n = 0;
   for (int i = 0; i < count; ++i) {
     const aql_w8a16_problem &p = problems[i];
     if (p.M == 0 || p.N == 0) continue;
+    const int64_t rows =
+        pieces ? aql::w8a16_pieces_tile_channels(p.K) : 4 * sh.tgroups * sh.cgroups;
     const int64_t nblk = (p.N + rows - 1) / rows, mblk = (p.M + 15) / 16;
     REQUIRE(blocks + nblk * mblk <= 0x7fffffffLL, AQL_ERR_SHAPE, "%s: too many tiles in total",
             fn);
@@ -387,6 +398,7 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
   h->tgroups = sh.tgroups;
   h->cgroups = sh.cgroups;
   h->xlds = sh.xlds;
+  h->kind = pieces ? 1 : 0;
   return ok();
 }
 
@@ -395,7 +407,10 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   REQUIRE(table, AQL_ERR_NULL, "%s: table must not be NULL", fn);
   const GroupHeader *h = static_cast<const GroupHeader *>(table);
   const bool m1 = h->mblocks == 0;
+  const bool pieces = h->kind == 1;
   REQUIRE(h->magic == kGroupMagic && h->version == 2 && h->count >= 0 && h->total_blocks >= 0 &&
+              (h->kind == 0 || (pieces && h->waves == 4 && h->mblocks == 0 && h->tgroups == 2 &&
+                                h->cgroups == 1 && h->xlds == 0)) &&
               (h->waves == 1 || h->waves == 2 || h->waves == 4 || h->waves == 8) &&
               (h->mblocks == 0 || h->mblocks == 1 || h->mblocks == 2 || h->mblocks == 4 ||
                h->mblocks == aql::kW8A16Skinny) &&
@@ -419,6 +434,10 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   sh.tgroups = h->tgroups;
   sh.cgroups = h->cgroups;
   sh.xlds = h->xlds;
+  if (pieces)
+    return launched(aql::launch_w8a16_m1p_grouped(dev_entries, h->count, h->total_blocks,
+                                                  (hipStream_t)stream),
+                    fn);
   return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, sh,
                                             (hipStream_t)stream),
                   fn);

@@ -70,4 +70,14 @@ static_assert(sizeof(W8A16GroupEntry) == 80, "table layout");
 hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
                                 const W8A16Shape &sh, hipStream_t st);
 
+// Grouped single-row GEMVs over contiguous 1 KB row pieces, for groups whose
+// problems all have M = 1 and kW8A16PiecesMinK <= K <= kW8A16PiecesMaxK. A
+// problem's tiles (workgroups of 4 waves) cover 32 channels when K <= 1024 and
+// 8 channels otherwise (w8a16_pieces_tile_channels).
+constexpr int64_t kW8A16PiecesMinK = 768;
+constexpr int64_t kW8A16PiecesMaxK = 4096;
+constexpr int64_t w8a16_pieces_tile_channels(int64_t K) { return K > 1024 ? 8 : 32; }
+hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
+                                    hipStream_t st);
+
 }  // namespace aql

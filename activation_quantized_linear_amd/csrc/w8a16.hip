@@ -657,6 +657,129 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_m1c(const uint16_t *__restrict
   y[n] = f32_to_bf16_rne(scale[n] * sum + bv);
 }
 
+// Grouped single-row GEMVs in the contiguous form of k_w8a16_m1c (1 KB row
+// pieces, lane l reading bytes 16 l .. 16 l + 15 of a piece). A workgroup has
+// 4 waves. For a problem with K <= 1024 each wave takes its own 8 channels and
+// their whole rows, one piece each (the lanes past K read nothing); for
+// 1024 < K <= 4096 the workgroup takes 8 channels and wave w piece w of each
+// row (a wave past the last piece idles), the waves' sums meeting in LDS.
+// Every row is read once and no byte past its end, where the 4 rows x 256 B
+// steps of the single-row tile over-read rows whose length is not a multiple
+// of 256. x comes straight from memory (the waves of a workgroup read the
+// same bytes of it, which the L1 serves) into fp32 registers.
+template <int B>
+__global__ __launch_bounds__(256) void k_w8a16_m1p_grouped(const W8A16GroupEntry *__restrict__ tab,
+                                                           int count) {
+  constexpr int W = 4, R = 8, NB = (R + B - 1) / B;
+  __shared__ float red[W][R];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int blk = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {  // last entry with begin <= blk
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab[mid].blk_begin <= blk) lo = mid;
+    else hi = mid - 1;
+  }
+  const W8A16GroupEntry &e = tab[lo];
+  const int64_t K = e.K, N = e.N;
+  const int local = blk - e.blk_begin;
+  const bool split = K > 1024;  // uniform
+  const int64_t n0 = split ? (int64_t)local * R : ((int64_t)local * W + wave) * R;
+  const int64_t k0 = split ? 1024LL * wave : 0;
+  const int64_t rem = N - n0;
+  const int64_t nrows = rem <= 0 ? 0 : (rem < R ? rem : R);
+  const bool active = nrows > 0 && k0 < K;  // uniform
+  const __amdgpu_buffer_rsrc_t rq = rsrc(nrows > 0 ? e.q + n0 * K : e.q, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(e.x, (uint32_t)(2 * K));
+  const int64_t kl = k0 + 16 * lane;
+  const int kk = kl < K ? (int)kl : -1;
+
+  float acc[R][2];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.0f;
+  if (active) {
+    auto issue = [&](int b, i32x4 *dst) {
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int r = b * B + u;
+        if (r < R) {
+          const int off = kk >= 0 ? (int)((uint32_t)r * (uint32_t)K + (uint32_t)kk) : OOB;
+          dst[u] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 2);
+        }
+      }
+    };
+    i32x4 wb0[B], wb1[B];
+    issue(0, wb0);
+    const int xo = kk >= 0 ? 2 * kk : OOB;
+    const i32x4 xr0 = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+    const i32x4 xr1 = __builtin_amdgcn_raw_buffer_load_b128(rx, kk >= 0 ? xo + 16 : OOB, 0, 0);
+    if (NB > 1) issue(1, wb1);
+    float xf[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xf[2 * i] = __uint_as_float((uint32_t)xr0[i] << 16);
+      xf[2 * i + 1] = __uint_as_float((uint32_t)xr0[i] & 0xffff0000u);
+      xf[8 + 2 * i] = __uint_as_float((uint32_t)xr1[i] << 16);
+      xf[8 + 2 * i + 1] = __uint_as_float((uint32_t)xr1[i] & 0xffff0000u);
+    }
+    auto consume = [&](int b, const i32x4 *src) {
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int r = b * B + u;
+        if (r < R) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int wv = src[u][c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[r][i & 1] = fmaf((float)(int8_t)(wv >> (8 * i)), xf[4 * c + i], acc[r][i & 1]);
+          }
+        }
+      }
+    };
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      __builtin_amdgcn_sched_barrier(0);
+      consume(b, (b & 1) ? wb1 : wb0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 2 < NB) issue(b + 2, (b & 1) ? wb1 : wb0);
+    }
+  }
+
+  // the transposing butterfly of k_w8a16_m1c: lane l ends with the sum of row l >> 3
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = acc[r][0] + acc[r][1];
+  float t4[4], t2[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) t4[j] = swap32_sum(v[j], v[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) t2[j] = swap16_sum(t4[j], t4[2 + j]);
+  const bool h3 = lane & 8;
+  float sum = (h3 ? t2[1] : t2[0]) + dpp_f32<kDppRowMirror>(h3 ? t2[0] : t2[1]);
+  sum += dpp_f32<kDppRowHalfMirror>(sum);
+  sum += dpp_f32<kDppQuadXor2>(sum);
+  sum += dpp_f32<kDppQuadXor1>(sum);
+  int row;
+  if (split) {
+    if ((lane & 7) == 0) red[wave][lane >> 3] = sum;
+    __syncthreads();
+    if (wave != 0 || lane >= R) return;
+    sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][lane];
+    row = lane;
+  } else {
+    if ((lane & 7) != 0) return;
+    row = lane >> 3;
+  }
+  const int64_t n = n0 + row;
+  if (n >= N) return;
+  const float bv = e.bias ? bf16_to_f32(e.bias[n]) : 0.0f;
+  e.y[n] = f32_to_bf16_rne(e.scale[n] * sum + bv);
+}
+
 // A few rows of x (2 <= M <= 4), contiguous form: the pieces and the wave
 // split of k_w8a16_m1c, with MR rows of x in registers as bf16 pairs and each
 // weight dword widened once (exact) and multiplied into the MR rows by
@@ -1095,6 +1218,13 @@ hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const
     hipLaunchKernelGGL((k_w8a16_m1c<4, 1, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
   else
     hipLaunchKernelGGL((k_w8a16_m1c<4, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
+                                    hipStream_t st) {
+  hipLaunchKernelGGL((k_w8a16_m1p_grouped<4>), dim3((unsigned)total_blocks), dim3(256), 0, st,
+                     dev_tab, count);
   return hipGetLastError();
 }
 

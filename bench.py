@@ -53,7 +53,7 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP64_PEAK_TFLOPS = 78.6      # MI355X fp64 vector (fused multiply-add counted as 2)
 MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = "k_w8a16_m1_grouped_smolvlm_decode_sweep_traffic.md"
+TRAFFIC_PROFILE = "k_w8a16_m1p_grouped_smolvlm_decode_sweep_traffic.md"
 HEADLINE_SOURCES = ("activation_quantized_linear_amd/csrc/w8a16.hip",
                     "activation_quantized_linear_amd/csrc/w8a16.h",
                     "activation_quantized_linear_amd/csrc/common.h")
@@ -845,7 +845,7 @@ def main():
             "unit": "GB/s",
             "frac": value / HBM_PEAK_GBS,
             "traffic": traffic_from_profile(TRAFFIC_PROFILE, HEADLINE_SOURCES),
-            "kernel": "k_w8a16_m1_grouped",
+            "kernel": "k_w8a16_m1p_grouped",
             "bytes_per_launch": step_bytes,
             "avg_launch_us": ms * 1e3,
             "launches_timed": args.steps,

@@ -310,6 +310,26 @@ def test_group_plan_validation():
     assert hdr[8] == 8192
     assert f(C.cast(_problems(3, {2: dict(K=16400)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
     assert hdr[8] == 0
+    # single rows with 768 <= K <= 4096 take the contiguous-pieces kernel: 4 waves,
+    # 32 channels a workgroup up to K = 1024, 8 above (N = 32: 1 and 4 workgroups)
+    assert f(C.cast(_problems(3, {0: dict(K=960), 1: dict(K=2560), 2: dict(K=768)}), C.c_void_p),
+             3, tp, nb) == aql.AQL_OK
+    hk = buf[:40].view(np.int32)
+    assert hk[9] == 1 and hk[4] == 4 and hk[5] == 0 and hk[7] == 1 and hk[8] == 0
+    assert hk[3] == 1 + 4 + 1
+    # one problem outside the range keeps the whole group on the tile kernels
+    assert f(C.cast(_problems(3, {0: dict(K=960), 1: dict(K=2560), 2: dict(K=4112)}), C.c_void_p),
+             3, tp, nb) == aql.AQL_OK
+    assert buf[:40].view(np.int32)[9] == 0
+    assert f(C.cast(_problems(3, {0: dict(K=960, M=2), 1: dict(K=2560)}), C.c_void_p),
+             3, tp, nb) == aql.AQL_OK
+    assert buf[:40].view(np.int32)[9] == 0
+    # a pieces table whose launch fields were altered is refused
+    assert f(C.cast(_problems(3, {0: dict(K=960), 1: dict(K=2560), 2: dict(K=768)}), C.c_void_p),
+             3, tp, nb) == aql.AQL_OK
+    tampered = buf.copy()
+    tampered[16:20] = np.array([2], np.int32).view(np.uint8)  # waves
+    assert L.aql_linear_w8a16_grouped(C.c_void_p(tampered.ctypes.data), A, None) == aql.AQL_ERR_PARAM
     # M > 1 tiles have one wave tile per workgroup and load x directly
     assert f(C.cast(_problems(3, {0: dict(M=5)}), C.c_void_p), 3, tp, nb) == aql.AQL_OK
     assert hdr[5] > 0 and hdr[7] == 1 and hdr[8] == 0

@@ -176,17 +176,19 @@ def test_choose_qparams_ties(K):
 
 
 def _plan_header(host_table):
-    """(count, total_blocks, waves, mblocks, tgroups, cgroups, xlds) of a plan."""
+    """(count, total_blocks, waves, mblocks, tgroups, cgroups, xlds, kind) of a plan."""
     h = host_table[:64].view(torch.int32).tolist()
     return dict(count=h[2], total_blocks=h[3], waves=h[4], mblocks=h[5], tgroups=h[6],
-                cgroups=h[7], xlds=h[8])
+                cgroups=h[7], xlds=h[8], kind=h[9])
 
 
-def test_w8a16_grouped_full_decode_sweep_paired_tiles():
+def test_w8a16_grouped_full_decode_sweep_pieces():
     """The 32-layer decode sweep exactly as the benchmark plans it (96 GEMVs,
-    weights quantized on the device): the plan pairs two 8-channel wave tiles
-    per workgroup (12,160 workgroups); every output of every GEMV is checked,
-    once eagerly and on three replays of a HIP graph."""
+    weights quantized on the device): single rows with 768 <= K <= 4096, so
+    the plan takes the contiguous-pieces kernel (up and gate, K = 960: 32
+    channels a workgroup; down, K = 2560: 8 channels whose three pieces go to
+    three waves), 8,960 workgroups; every output of every GEMV is checked, once
+    eagerly and on three replays of a HIP graph."""
     layers = workloads.smolvlm(seed=0)
     F, H = workloads.SMOLVLM_FFN, workloads.SMOLVLM_HIDDEN
     probs, refs = [], []
@@ -202,8 +204,8 @@ def test_w8a16_grouped_full_decode_sweep_paired_tiles():
     host_t, dev_t = aql.aql_w8a16_group_plan(probs)
     h = _plan_header(host_t)
     say("sweep plan", h)
-    assert h["mblocks"] == 0 and h["cgroups"] == 2 and h["count"] == 96
-    assert h["total_blocks"] == 32 * (2 * (F // 16) + H // 16) == 12160
+    assert h["kind"] == 1 and h["mblocks"] == 0 and h["waves"] == 4 and h["count"] == 96
+    assert h["total_blocks"] == 32 * (2 * (F // 32) + H // 8) == 8960
     expect = [oracle.linear_w8a16(bits(xc), host(p[1]), host(p[2])) for p, xc in zip(probs, refs)]
 
     def check(what):
@@ -227,6 +229,38 @@ def test_w8a16_grouped_full_decode_sweep_paired_tiles():
         check(f"graph replay {rep}")
 
 
+@pytest.mark.parametrize("dense", [False, True])
+def test_w8a16_grouped_pieces_ragged(dense):
+    """The contiguous-pieces kernel at the edges of its range: K = 768 (its
+    smallest), 1024 (one whole piece), 1040 (a second piece of 16 bytes), 2064,
+    4096 (four pieces, one per wave), with N leaving the last workgroup's waves
+    partly or wholly past the last channel (N = 1, 9, 33, 41, 2570); with
+    `dense` the weights are all +-127 and x is large, so every product is at
+    the top of its range."""
+    g = workloads.gen(713 + dense)
+    shapes = [(2570, 768), (9, 1024), (33, 1040), (1, 2064), (41, 4096), (2560, 960),
+              (300, 2560), (8, 4096), (7, 1024)]
+    probs, refs = [], []
+    for N, K in shapes:
+        w = workloads.small_matrix(g, N, K, std=0.02)
+        if dense:
+            w = torch.where(w >= 0, 1.0, -1.0)
+        x = workloads.small_matrix(g, 1, K, std=30.0 if dense else 1.0).to(torch.bfloat16)
+        q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        y = torch.full((1, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        probs.append((dev(x), q, s, None, y))
+        refs.append(x)
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    h = _plan_header(host_t)
+    say("pieces ragged plan", h)
+    assert h["kind"] == 1
+    assert h["total_blocks"] == sum(-(-N // (8 if K > 1024 else 32)) for N, K in shapes)
+    aql.aql_linear_w8a16_grouped(host_t, dev_t)
+    for (x, q, s, _, y), xc in zip(probs, refs):
+        yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s), None)
+        check_float(host(y.float()), yref, tol, BF16, f"pieces ragged {tuple(q.shape)}")
+
+
 def test_w8a16_grouped_paired_tiles_ragged_n():
     """A single-row group past 8,192 wave tiles (so tiles are paired per
     workgroup) whose channel counts leave the second tile of a pair partly
@@ -245,7 +279,7 @@ def test_w8a16_grouped_paired_tiles_ragged_n():
     host_t, dev_t = aql.aql_w8a16_group_plan(probs)
     h = _plan_header(host_t)
     say("ragged paired plan", h)
-    assert h["mblocks"] == 0 and h["cgroups"] == 2
+    assert h["kind"] == 0 and h["mblocks"] == 0 and h["cgroups"] == 2
     assert h["total_blocks"] == sum(-(-N // 16) for N, _ in shapes)
     aql.aql_linear_w8a16_grouped(host_t, dev_t)
     for (x, q, s, _, y), xc in zip(probs, refs):

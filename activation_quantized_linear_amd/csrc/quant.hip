@@ -40,6 +40,18 @@ __device__ __forceinline__ int wcode(float w, float s, float lo) {
   return (int)clamp_code(rintf(w / s), lo, 127.0f);
 }
 
+// The same code from r = 1 / s (IEEE, s normal): |w / s| <= 128 here, so
+// t = w r is within 2^-16 of w / s (r's relative error and t's rounding, 2^-17
+// each at most) and the IEEE quotient within 2^-18 of it. Unless t lies within
+// 2^-10 of a half-integer, both fall strictly inside the same rounding interval
+// and rint(t) is rint(w / s); those few take the division itself.
+__device__ __forceinline__ int wcode_r(float w, float s, float r, float lo) {
+  const float t = w * r;
+  float c = rintf(t);
+  if (fabsf(t - c) > 0.5f - 0x1p-10f) c = rintf(w / s);
+  return (int)clamp_code(c, lo, 127.0f);
+}
+
 // TPR threads own one row (TPR = 64: a wave per row, 4 rows per workgroup;
 // TPR = 256: the workgroup per row). VPT float4 vectors per thread stay in
 // registers between the absmax and the quantization; VPT = 0 re-reads the
@@ -71,14 +83,28 @@ __global__ __launch_bounds__(256) void k_quantize_weight_int8(
     }
     amax = group_reduce_max<TPR>(amax, red_f);
     const float s = (amax == 0.0f) ? 1.0f : amax / den;
+    const float r = 1.0f / s;
+    if (s >= 0x1p-126f) {  // uniform: the reciprocal path needs a normal s
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int64_t j = t + (int64_t)i * TPR;
-      if (active && j < nvec) {
-        const int a = wcode(v[i].x, s, lo), b = wcode(v[i].y, s, lo);
-        const int c = wcode(v[i].z, s, lo), d = wcode(v[i].w, s, lo);
-        qrow[j] = pack4(a, b, c, d);
-        sum += a + b + c + d;
+      for (int i = 0; i < VPT; ++i) {
+        const int64_t j = t + (int64_t)i * TPR;
+        if (active && j < nvec) {
+          const int a = wcode_r(v[i].x, s, r, lo), b = wcode_r(v[i].y, s, r, lo);
+          const int c = wcode_r(v[i].z, s, r, lo), d = wcode_r(v[i].w, s, r, lo);
+          qrow[j] = pack4(a, b, c, d);
+          sum += a + b + c + d;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int64_t j = t + (int64_t)i * TPR;
+        if (active && j < nvec) {
+          const int a = wcode(v[i].x, s, lo), b = wcode(v[i].y, s, lo);
+          const int c = wcode(v[i].z, s, lo), d = wcode(v[i].w, s, lo);
+          qrow[j] = pack4(a, b, c, d);
+          sum += a + b + c + d;
+        }
       }
     }
     sum = group_reduce_sum<TPR>(sum, red_i);

@@ -11,8 +11,9 @@ namespace aql {
 // xq in the permute8 order, larger M the bf16 differences xd (see
 // launch_choose_qparams_rows).
 constexpr int64_t kQ4StreamMaxM = 16;
-// M <= kQ4FewMaxM and K <= kQ4FewMaxK: the few-rows kernel (dot4 group sums,
-// contiguous weight pieces); the codes are in the permute8 order as well
+// M <= kQ4FewMaxM and K <= kQ4FewMaxK: the few-rows kernel (group sums on the
+// matrix cores, all of a wave's K in flight); the codes are in the permute8
+// order as well
 constexpr int64_t kQ4FewMaxM = 4;
 constexpr int64_t kQ4FewMaxK = 8192;
 struct Q4Args {

@@ -32,6 +32,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_
                                            0x00020000);
 }
 
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (n < 64)
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 __device__ __forceinline__ long unpack_q4x8(uint32_t w) {
   const uint32_t even = (w << 4) & 0xF0F0F0F0u;
   const uint32_t odd = w & 0xF0F0F0F0u;
@@ -206,22 +209,7 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_stream(Q4Args p) {
   }
 }
 
-// ------------------------------------------------------- few rows (M <= 4)
-// The weights stream as contiguous 1 KB pieces of one channel's row per wave
-// instruction (lane l holds 32-k group 64 p + l whole), the group scales as
-// 256-byte pieces beside them; all of a wave's pieces are requested before
-// anything else, so the whole stream is in flight from the start. The
-// workgroup copies the M rows of codes (permute8 order, from the qparams
-// kernel) into LDS with buffer-to-LDS loads. Each group's sum is formed exactly
-// by signed 4-way byte dot products (v_dot4_i32_i8) of the codes with the
-// nibbles unpacked as 16 c:
-//     A16 = sum_k xq (16 c) - zp * sum_k (16 c)     (|A16| < 2^24, exact)
-// and folded with one FMA, f += gs * A16; y = s * (f / 16) + bias. A wave owns
-// RW channels over all of K, so it needs no other wave's partial sums; its
-// lanes' partials are summed by a transposing butterfly (each exchange step
-// halves the values a lane carries) of DPP moves and lane-half swaps.
-// (Forming the row qparams inside this kernel instead, in every workgroup,
-// measured slower: 12.5 vs 11.3 us at M = 4, K = 4096, N = 11008.)
+// Cross-lane helpers of the few-rows kernel.
 template <int CTRL>
 __device__ __forceinline__ float q4_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -237,150 +225,154 @@ __device__ __forceinline__ float q4_swap16_sum(float a, float b) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-template <int W, int RW, int NP>
-__global__ __launch_bounds__(64 * W) void k_dq8ca_q4_few(Q4Args p) {
-  constexpr int V = 4 * RW;  // partial sums per lane: RW channels x 4 rows
-  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // [M][K] codes, permute8 order
-  __shared__ float qs_s[4], qs_z[4];
+// ------------------------------------------- few rows on the matrix cores (M <= 4)
+// The weights stream as TG x 4 channel rows x 256 contiguous bytes per wave
+// instruction (lane 4 b + j: the whole 32-k group 16 s + b of channel 4 tg + j),
+// and every step s of the wave's K is requested, with its group scales, before
+// any arithmetic. Group sums are formed on the matrix cores as in the streaming
+// kernel: v_mfma_i32_4x4x4_i8 block b multiplies the 4 rows of x codes of its
+// group (A row i = lane 4 b + i) by the 4 channels' nibbles of that group
+// unpacked as 16 c (B column j = lane 4 b + j), 8 MFMAs of 4 k, and 8 more
+// against an all-ones A give 16 x the group's code sum. Lane 4 b + j then holds
+// its channel's exact A16 for the 4 rows and folds each with one FMA,
+// f += gs * (A16 - zp * gsum16): the vector ALU only unpacks and folds. The 16
+// groups of a step (lanes j, j + 4, ..., j + 60) are summed at the end by two
+// transposing exchanges (lane bits 5 and 4) and two row-rotation adds (bits 3
+// and 2).
+//
+// The x codes (from the qparams kernel) are copied into LDS first, by buffer
+// loads that write LDS, ahead of the weights: row i at i * xpitch (xpitch = 64
+// mod 256) holds the first 16 bytes of every group, then the second 16, so that
+// the 16 lanes of a read (4 rows x 4 groups) cover distinct banks. (Forming the
+// row qparams and codes inside this kernel, every workgroup for itself, measured
+// slower: 12.8 vs 8.8 us at M = 4, K = 4096, N = 11008; the workgroups that
+// start last find their x reads queued behind the weight stream.)
+template <int W, int TG, int NS>
+__global__ __launch_bounds__(64 * W) void k_dq8ca_q4_fm(Q4Args p, int xpitch) {
+  constexpr int V = 4 * TG;  // partial sums per lane: TG x 4 channels' rows 0..3
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];  // M rows of xpitch bytes
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 3, blk = lane >> 2;
   const int64_t M = p.M, N = p.N, K = p.K, G = K / 32, KB = K / 2;
-  const int64_t n0 = (int64_t)blockIdx.x * (W * RW) + (int64_t)wave * RW;
+  const int64_t n0 = ((int64_t)blockIdx.x * W + wave) * (4 * TG);
   const int64_t rem = N - n0;
-  const int64_t nrows = rem <= 0 ? 0 : (rem < RW ? rem : RW);
+  const int64_t nrows = rem <= 0 ? 0 : (rem < 4 * TG ? rem : 4 * TG);
   const __amdgpu_buffer_rsrc_t rq = rsrc(nrows > 0 ? p.q4 + n0 * KB : p.q4, (uint32_t)(nrows * KB));
   const __amdgpu_buffer_rsrc_t rg = rsrc(nrows > 0 ? p.gs + n0 * G : p.gs, (uint32_t)(nrows * G * 4));
-  i32x4 w[NP][RW];
-  float gsv[NP][RW];
-#pragma unroll
-  for (int pc = 0; pc < NP; ++pc) {
-    const int64_t g = 64LL * pc + lane;
-    const bool gin = g < G;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      w[pc][r] = __builtin_amdgcn_raw_buffer_load_b128(
-          rq, gin ? (int)((uint32_t)r * (uint32_t)KB + 16u * (uint32_t)g) : OOB, 0, 2);
-      gsv[pc][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-          rg, gin ? (int)(4u * ((uint32_t)r * (uint32_t)G + (uint32_t)g)) : OOB, 0, 2));
-    }
-  }
-  {
-    // LDS row m holds the first 16 code bytes of every group, then the second
-    // 16 (unit u = 16-byte slot: half h = u / G, group u % G), so a lane's two
-    // reads of its group are each contiguous across the wave (no bank conflicts)
-    const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, (uint32_t)(M * K));
-    const int nch = (int)((M * K + 1023) >> 10);
-    const uint32_t base = (uint32_t)(uintptr_t)xl;
-    for (int c = wave; c < nch; c += W) {
-      const int u = 64 * c + lane, m = (int)(u / (2 * G)), rest = (int)(u % (2 * G));
-      const int h = (int)(rest / G), gg = (int)(rest % G);
-      const int src = m < M ? (int)((int64_t)m * K + 32LL * gg + 16 * h) : OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + 1024u * c), 16, src, 0,
-          0, 0);
-    }
-    if (wave == 0 && lane < 4) {
-      qs_s[lane] = lane < M ? p.xs[lane] : 0.0f;
-      qs_z[lane] = lane < M ? (float)p.xz[lane] : 0.0f;
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies landed
-  }
-  __syncthreads();
-  int zpn[4];
-  float sm[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    zpn[m] = -(int)qs_z[m];
-    sm[m] = qs_s[m];
-  }
+  const int nst = (int)((KB + 255) >> 8);  // steps of 512 k (256 packed bytes a row)
 
-  float f[RW][4];
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) f[r][m] = 0.0f;
-#pragma unroll
-  for (int pc = 0; pc < NP; ++pc) {
-    const int64_t g = 64LL * pc + lane;
-    i32x4 xv[4][2];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // rows past M read row 0 (their sums are never written)
-      const int xo = (g < G ? (int)(16 * g) : 0) + (m < M ? m * (int)K : 0);
-      xv[m][0] = *reinterpret_cast<const i32x4 *>(xl + xo);
-      xv[m][1] = *reinterpret_cast<const i32x4 *>(xl + xo + 16 * (int)G);
+  // ---- x codes into LDS first (they gate the arithmetic), then the weights
+  {
+    const __amdgpu_buffer_rsrc_t rx = rsrc(p.xq, (uint32_t)(M * K));
+    const int cpr = (int)((K + 1023) >> 10);  // 1 KB copies per row
+    const uint32_t base = (uint32_t)(uintptr_t)xl;
+    for (int c = wave; c < (int)M * cpr; c += W) {
+      const int i = c / cpr, u = 64 * (c % cpr) + lane;  // unit u: half u / G, group u % G
+      const int h = (int)(u / G), g = (int)(u % G);
+      const int src = u < 2 * G ? (int)((int64_t)i * K + 32 * g + 16 * h) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(i * xpitch + 1024 * (c % cpr))),
+          16, src, 0, 0, 0);
     }
+  }
+  __asm__ volatile("" ::: "memory");
+
+  i32x4 q[NS][TG];
+  float gsv[NS][TG];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
+  for (int s = 0; s < NS; ++s) {
+    // this lane's group lies before K (steps past the last, or the lanes of a
+    // last step past K, read 0: zero codes and a zero group scale add nothing)
+    const bool kin = s < nst && 256 * s + 16 * blk < KB;
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
+      const uint32_t row = (uint32_t)(4 * tg + j);
+      q[s][tg] = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, kin ? (int)(row * (uint32_t)KB + 256u * s + 16u * blk) : OOB, 0, 2);
+      gsv[s][tg] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(
+                     rg, kin ? (int)(4u * (row * (uint32_t)G + 16u * s + blk)) : OOB, 0, 2));
+    }
+  }
+  // the copies of x were issued before the 2 TG NS weight loads: wait for them
+  // only, then for the other waves' copies
+  static_assert(2 * TG * NS < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * TG * NS));
+  // row scales and -zp (0 past M) by scalar loads: a vector load here would
+  // wait for every weight load
+  const __attribute__((address_space(4))) int32_t *xzc =
+      (const __attribute__((address_space(4))) int32_t *)(uintptr_t)p.xz;
+  const __attribute__((address_space(4))) float *xsc =
+      (const __attribute__((address_space(4))) float *)(uintptr_t)p.xs;
+  int zpn[4];
+  float sc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int v = xzc[r < M ? r : 0];
+    sc[r] = xsc[r < M ? r : 0];
+    zpn[r] = r < M ? -v : 0;
+  }
+  __builtin_amdgcn_s_barrier();
+  // rows of x past M read row 0 (their sums are never written)
+  const char *xrow = reinterpret_cast<const char *>(xl) + (j < M ? j : 0) * xpitch + 16 * blk;
+
+  float t[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) t[i] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (s >= nst) continue;  // uniform
+    i32x4 xv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      xv[h] = *reinterpret_cast<const i32x4 *>(xrow + h * 16 * (int)G + 256 * s);
+#pragma unroll
+    for (int tg = 0; tg < TG; ++tg) {
       int wq[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t u = (uint32_t)w[pc][r][e];
-        wq[2 * e] = (int)((u << 4) & 0xF0F0F0F0u);  // k = 8e + 0, 2, 4, 6, as 16 c
-        wq[2 * e + 1] = (int)(u & 0xF0F0F0F0u);     // k = 8e + 1, 3, 5, 7
+        const uint32_t w = (uint32_t)q[s][tg][e];
+        wq[2 * e] = (int)((w << 4) & 0xF0F0F0F0u);  // k = 8e + 0, 2, 4, 6, as 16 c
+        wq[2 * e + 1] = (int)(w & 0xF0F0F0F0u);     // k = 8e + 1, 3, 5, 7
       }
-      int gsum16 = 0;
+      i32x4 cs = {0, 0, 0, 0}, a = {0, 0, 0, 0};
 #pragma unroll
-      for (int d = 0; d < 8; ++d) gsum16 = __builtin_amdgcn_sdot4(0x01010101, wq[d], gsum16, false);
+      for (int d = 0; d < 8; ++d) cs = __builtin_amdgcn_mfma_i32_4x4x4i8(0x01010101, wq[d], cs, 0, 0, 0);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        int acc = 0;
+      for (int d = 0; d < 8; ++d)
+        a = __builtin_amdgcn_mfma_i32_4x4x4i8(xv[d >> 2][d & 3], wq[d], a, 0, 0, 0);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) acc = __builtin_amdgcn_sdot4(xv[m][d >> 2][d & 3], wq[d], acc, false);
-        // |zp| <= 128 and |gsum16| <= 4096: a 24-bit product
-        f[r][m] += gsv[pc][r] * (float)(acc + __mul24(zpn[m], gsum16));
-      }
+      for (int v = 0; v < 4; ++v)  // |zp| <= 128 and |gsum16| <= 4096: a 24-bit product
+        t[4 * tg + v] += gsv[s][tg] * (float)(a[v] + __mul24(zpn[v], cs[0]));
     }
   }
 
-  // ---- sum the V = 4 RW partials over the 64 lanes: log2(V) transposing
-  // exchange steps (lane bits 5, 4, 3, ...), then plain ones; lane l ends with
-  // value index l >> (6 - log2 V)
-  float t[V];
+  // ---- sum over lane bits 5..2 (the 16 groups): the transposing exchanges over
+  // bits 5 and 4 halve the values a lane carries, rotations by 8 and 4 lanes
+  // within each row of 16 add over bits 3 and 2
 #pragma unroll
-  for (int r = 0; r < RW; ++r)
+  for (int i = 0; i < V / 2; ++i) t[i] = q4_swap32_sum(t[i], t[V / 2 + i]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) t[4 * r + m] = f[r][m];
-  static_assert(V == 8 || V == 16 || V == 32, "RW in {2, 4, 8}");
-  constexpr int LV = V == 8 ? 3 : (V == 16 ? 4 : 5);
+  for (int i = 0; i < V / 4; ++i) t[i] = q4_swap16_sum(t[i], t[V / 4 + i]);
 #pragma unroll
-  for (int j = 0; j < V / 2; ++j) t[j] = q4_swap32_sum(t[j], t[V / 2 + j]);
-#pragma unroll
-  for (int j = 0; j < V / 4; ++j) t[j] = q4_swap16_sum(t[j], t[V / 4 + j]);
-  // lane bit 3 by the row mirror, bit 2 by the half-row mirror, bits 1 and 0
-  // by quad exchanges
-  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-#pragma unroll
-  for (int j = 0; j < V / 8; ++j) {
-    const float keep = b3 ? t[V / 8 + j] : t[j], send = b3 ? t[j] : t[V / 8 + j];
-    t[j] = keep + q4_dpp<0x140>(send);
+  for (int i = 0; i < V / 4; ++i) {
+    t[i] += q4_dpp<0x128>(t[i]);  // row_ror:8
+    t[i] += q4_dpp<0x124>(t[i]);  // row_ror:4
   }
-  float sum;
-  if constexpr (LV == 3) {
-    sum = t[0] + q4_dpp<0x141>(t[0]);
-    sum += q4_dpp<0x4E>(sum);
-    sum += q4_dpp<0xB1>(sum);
-  } else {
+  if ((lane & 12) != 0) return;
+  // lane l holds, for i < TG, value index (l >> 5) V/2 + ((l >> 4) & 1) V/4 + i
 #pragma unroll
-    for (int j = 0; j < V / 16; ++j) {
-      const float keep = b2 ? t[V / 16 + j] : t[j], send = b2 ? t[j] : t[V / 16 + j];
-      t[j] = keep + q4_dpp<0x141>(send);
+  for (int i = 0; i < TG; ++i) {
+    const int idx = (lane >> 5) * (V / 2) + ((lane >> 4) & 1) * (V / 4) + i;
+    const int tg = idx >> 2, m = idx & 3;
+    const int64_t n = n0 + 4 * tg + j;
+    if (m < M && n < N) {
+      const float bv = p.bias ? p.bias[n] : 0.0f;
+      const float sm = m == 0 ? sc[0] : (m == 1 ? sc[1] : (m == 2 ? sc[2] : sc[3]));
+      p.y[m * N + n] = sm * (t[i] * 0.0625f) + bv;
     }
-    if constexpr (LV == 4) {
-      sum = t[0] + q4_dpp<0x4E>(t[0]);
-    } else {
-      const float keep = b1 ? t[1] : t[0], send = b1 ? t[0] : t[1];
-      sum = keep + q4_dpp<0x4E>(send);
-    }
-    sum += q4_dpp<0xB1>(sum);
   }
-  if ((lane & ((64 >> LV) - 1)) != 0) return;
-  const int idx = lane >> (6 - LV);
-  const int r = idx >> 2, m = idx & 3;
-  const int64_t n = n0 + r;
-  if (m >= M || n >= N) return;
-  const float bv = p.bias ? p.bias[n] : 0.0f;
-  p.y[m * N + n] = sm[m] * (sum * 0.0625f) + bv;
 }
 
 // ----------------------------------------------------------------- tiled
@@ -731,20 +723,30 @@ void launch_tiled(const Q4Args &a, hipStream_t st) {
                      C::LDS, st, a, tiles_m, tiles_n);
 }
 
+// Few rows on the matrix cores: 4 waves of 4 channels, all of K in flight (NS
+// steps of 512 k). K = 4096, N = 11008: 8.8 us at M = 4 and 8.0 at M = 1,
+// against 10.0 and 8.2 for group sums formed by 4-byte dot products on the
+// vector ALU (1 KB weight pieces); 2 channel groups a wave or 8 waves a
+// workgroup measured slower.
+void launch_fm(const Q4Args &a, hipStream_t st) {
+  constexpr int W = 4, TG = 1;
+  const dim3 grid((unsigned)((a.N + 4 * TG * W - 1) / (4 * TG * W)));
+  const int xpitch = (int)((a.K + 1023) / 1024 * 1024 + 64);
+  const size_t lds = (size_t)(a.M * xpitch);
+#define AQL_FM(ns) hipLaunchKernelGGL((k_dq8ca_q4_fm<W, TG, ns>), grid, dim3(64 * W), lds, st, a, xpitch)
+  if (a.K <= 512) AQL_FM(1);
+  else if (a.K <= 1024) AQL_FM(2);
+  else if (a.K <= 2048) AQL_FM(4);
+  else if (a.K <= 4096) AQL_FM(8);
+  else AQL_FM(16);
+#undef AQL_FM
+}
+
 }  // namespace
 
 hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
   if (a.M <= kQ4FewMaxM && a.K <= kQ4FewMaxK) {
-    // 4 waves of 2 channels; 1, 2 or 4 pieces of 1 KB per channel row
-    constexpr int W = 4, RW = 2;
-    const dim3 grid((unsigned)((a.N + W * RW - 1) / (W * RW)));
-    const size_t lds = (size_t)((a.M * a.K + 1023) / 1024 * 1024);
-    if (a.K <= 2048)
-      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 1>), grid, dim3(64 * W), lds, st, a);
-    else if (a.K <= 4096)
-      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 2>), grid, dim3(64 * W), lds, st, a);
-    else
-      hipLaunchKernelGGL((k_dq8ca_q4_few<W, RW, 4>), grid, dim3(64 * W), lds, st, a);
+    launch_fm(a, st);
   } else if (a.M <= kQ4StreamMaxM) {
     // 8-channel tiles for M <= 2, 16 otherwise; waves per workgroup (splitting
     // K) only while the wave-tiles are fewer than ~384: these waves are short

@@ -433,10 +433,11 @@ def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
                                    (4, 11008, 4096)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_dq8ca_q4_few_rows(M, N, K, with_bias):
-    """M <= 4 and K <= 8192 run the few-rows 4-bit kernel (dot4 group sums on
-    1, 2 or 4 contiguous 1 KB pieces per channel row, the last partly past K;
-    N not a multiple of 8); K = 8224 takes the general streaming kernel. Rows:
-    all zero, one-sided positive, one-sided negative, a saturating outlier."""
+    """M <= 4 and K <= 8192 run the few-rows 4-bit kernel (group sums on the
+    4x4x4 int8 matrix-core blocks, 1, 2, 4, 8 or 16 steps of 512 k in flight,
+    the last partly past K; N not a multiple of 16); K = 8224 takes the general
+    streaming kernel. Rows: all zero, one-sided positive, one-sided negative, a
+    saturating outlier."""
     say("dq8ca q4 small M", M, N, K, with_bias)
     g = workloads.gen(660 + M + N + K)
     x = workloads.small_matrix(g, M, K)

@@ -37,6 +37,7 @@ AQL_W_Q4GSW = 1
 AQL_OP_Q8TA_Q8CSW = 1
 AQL_OP_DQ8CA = 2
 AQL_OP_GPTQ_INT8 = 3
+AQL_OP_W8A16 = 4
 AQL_MAX_K_INT8 = 65536
 AQL_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -62,7 +63,7 @@ _SIGS = {
     "aql_choose_qparams_rows": ([_p, _i64, _i64, _p, _p, _p, _p], _int),
     "aql_quantize_act_per_tensor": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p, _p],
                                     _int),
-    "aql_linear_w8a16": ([_p, _i64, _i64, _p, _p, _p, _i64, _p, _p], _int),
+    "aql_linear_w8a16": ([_p, _i64, _i64, _p, _p, _p, _i64, _p, _p, _sz, _p], _int),
     "aql_linear_q8ta_q8csw": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p, _p, _p,
                                _i64, _p, _p, _sz, _p], _int),
     "aql_linear_q8ta_q8csw_noalloc": ([_p, _i64, _i64, _f32, _i32, _int, _f32, _i32, _p, _p,
@@ -222,8 +223,10 @@ def aql_quantize_act_per_tensor(x, s1, z1, two_pass=False, s2=1.0, z2=0, xq1=Non
 # -------------------------------------------------------------------- linears
 
 
-def aql_linear_w8a16(x, q, scale, bias=None, y=None):
-    """x bfloat16 [M, K], q int8 [N, K], scale float32 [N], bias bfloat16 [N] -> y bfloat16 [M, N]."""
+def aql_linear_w8a16(x, q, scale, bias=None, y=None, workspace=None):
+    """x bfloat16 [M, K], q int8 [N, K], scale float32 [N], bias bfloat16 [N] -> y bfloat16 [M, N].
+    workspace: uint8 device tensor; allocated here when the shape can use one
+    (aql_workspace_bytes(AQL_OP_W8A16, ...) > 0) and none is given."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     _need(q, "q", torch.int8, 2, dev)
@@ -236,9 +239,13 @@ def aql_linear_w8a16(x, q, scale, bias=None, y=None):
         _need(bias, "bias", torch.bfloat16, 1, dev)
         _shape(bias, "bias", (N,))
     y = _out(y, "y", (M, N), torch.bfloat16, dev)
+    nbytes = aql_workspace_bytes(AQL_OP_W8A16, M, N, K)
+    ws = None
+    if workspace is not None or nbytes > 0:
+        ws = _workspace(workspace, nbytes, dev)
     _check("aql_linear_w8a16",
            _lib.aql_linear_w8a16(_ptr(x), M, K, _ptr(q), _ptr(scale), _ptr(bias), N, _ptr(y),
-                                 _stream(dev)))
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
     return y
 
 

@@ -230,6 +230,10 @@ size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > aql::kGptqMaxBlock || K > AQL_MAX_K_INT8) return 0;
     return aql::gptq_workspace_bytes(N, K, M);
   }
+  if (op == AQL_OP_W8A16) {
+    if (M < kW8A16GemmMinM || K > (1LL << 22) || N == 0) return 0;
+    return aql::w8a16_gemm_part_bytes(M, N, K);
+  }
   return 0;
 }
 
@@ -310,16 +314,18 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
 
 int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
-                     void *stream) {
+                     void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "aql_linear_w8a16";
   if (int e = check_w8a16(fn, x, M, K, q, scale, bias, N, y)) return e;
+  REQUIRE(aligned16(ws), AQL_ERR_ALIGN, "%s: ws must be 16-byte aligned", fn);
   if (M == 0 || N == 0) return ok();
   if (int e = check_device(fn)) return e;
   // M-dispatch (flashrt schemes, W8A16Decode: the decode band goes to the
   // weight-streaming kernel): from 64 rows on, the tiled bf16-MFMA GEMM reads
   // each weight once per 64 or 128 rows instead of once per 16.
   if (M >= kW8A16GemmMinM && K <= (1LL << 22))
-    return launched(aql::launch_w8a16_gemm(x, M, K, q, scale, bias, N, y, (hipStream_t)stream),
+    return launched(aql::launch_w8a16_gemm(x, M, K, q, scale, bias, N, y, static_cast<float *>(ws),
+                                           ws ? ws_bytes : 0, (hipStream_t)stream),
                     fn);
   return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
 }

@@ -358,27 +358,41 @@ struct WideLds {
   static constexpr int TLD = BNW + 8;           // bf16 per staged output row
   static constexpr int TILE = BM * TLD * 2;
   static constexpr int BYTES = RING > TILE ? RING : TILE;
+  static constexpr int TLDF = BNW + 4;          // fp32 per staged partial-sum row (split K)
+  static constexpr int TILEF = BM * TLDF * 4;
+  static constexpr int BYTES_SPLIT = RING > TILEF ? RING : TILEF;
 };
 
 // SG = 4: a 4-stage ring, one workgroup a CU. SG = 2: a 2-stage ring in
 // 64 KB, so two workgroups share a CU and each covers the other's waits at
 // the stage barrier (from 512 tiles on, where every CU gets two).
-template <int SG>
+//
+// SPLIT: the grid is tiles x S units, unit (tile, sp) taking the ks stages of
+// 64 k from sp * ks (a multiple of SG); it writes its fp32 partial sums, before
+// any scale, to part[sp][M][N], which k_w8a16_splitk_reduce adds. This serves
+// the grids of few tiles and long rows (M = 512, K = 14336, N = 4096: 64 tiles
+// of 4 x 3584 k instead of 256 tiles of 64 x 128 over the whole row), where
+// every CU otherwise streams the whole of K for a small tile: the operand
+// bytes per CU halve.
+template <int SG, bool SPLIT>
 __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const uint16_t *__restrict__ x,
                                                          const int8_t *__restrict__ q,
                                                          const float *__restrict__ scale,
                                                          const uint16_t *__restrict__ bias,
                                                          uint16_t *__restrict__ y, int64_t M,
                                                          int64_t N, int64_t K, int tiles_m,
-                                                         int tiles_n) {
+                                                         int tiles_n, float *__restrict__ part,
+                                                         int ks) {
   using L = WideLds<SG>;
   constexpr int BM = L::BM, BNW = L::BNW, NL = 4;  // loads per wave per stage
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int nt = tiles_m * tiles_n;
+  const int nu = (int)gridDim.x;  // nt tiles x (nu / nt) splits of K
   const int lin = blockIdx.x;
-  int tile = lin;
-  if ((nt & 7) == 0) tile = (lin & 7) * (nt >> 3) + (lin >> 3);
+  int unit = lin;
+  if ((nu & 7) == 0) unit = (lin & 7) * (nu >> 3) + (lin >> 3);
+  const int tile = unit % nt, sp = unit / nt;
   const int tn = tile / tiles_m, tm = tile % tiles_m;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BNW;
 
@@ -472,10 +486,12 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
     }
   };
 
-  const int nk = (int)((K + BK - 1) / BK);
+  const int nk_all = (int)((K + BK - 1) / BK);
+  const int k0 = SPLIT ? sp * ks : 0;  // stages [k0, nk) of this unit
+  const int nk = SPLIT ? (k0 + ks < nk_all ? k0 + ks : nk_all) : nk_all;
 #pragma unroll
-  for (int s = 0; s < SG - 1; ++s) issue(s);
-  int kt = 0;
+  for (int s = 0; s < SG - 1; ++s) issue(k0 + s);
+  int kt = k0;
   auto step = [&](int k) {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (SG - 2)));
     __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
@@ -508,6 +524,35 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
+
+  if constexpr (SPLIT) {
+    // the partial sums through LDS, then whole rows of 1 KB: 64 lanes x 16 B
+    float *tf = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tf[(i * 16 + 4 * g + v) * L::TLDF + wn * 32 + j * 16 + r] = acc[i][j][v];
+    __syncthreads();
+    const bool vec4 = (N & 3) == 0;
+    float *pb = part + (int64_t)sp * M * N;
+    for (int u = tid; u < BM * 64; u += 512) {
+      const int row = u >> 6, c = u & 63;
+      const int64_t m = m0 + row, n = n0 + 4 * c;
+      if (m >= M || n >= N) continue;
+      const f32x4 val = *reinterpret_cast<const f32x4 *>(tf + row * L::TLDF + 4 * c);
+      float *dst = pb + m * N + n;
+      if (vec4) {
+        *reinterpret_cast<f32x4 *>(dst) = val;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) dst[e] = val[e];
+      }
+    }
+    return;
+  }
 
   // scale + bias + bf16 into the LDS output tile; acc[i][j] lane holds
   // D[4g + v][r] of MFMA tile (i, j): row m, column n.
@@ -544,20 +589,96 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
   }
 }
 
+// y[m, n] = bf16(scale[n] (part[0][m][n] + ... + part[S-1][m][n]) + bias[n]),
+// the sum in split order; a thread takes 8 consecutive outputs of a row.
+__global__ __launch_bounds__(256) void k_w8a16_splitk_reduce(const float *__restrict__ part, int S,
+                                                            int64_t M, int64_t N,
+                                                            const float *__restrict__ scale,
+                                                            const uint16_t *__restrict__ bias,
+                                                            uint16_t *__restrict__ y) {
+  const int64_t ng = (N + 7) / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * ng) return;
+  const int64_t m = i / ng, n = (i % ng) * 8;
+  const int cnt = N - n < 8 ? (int)(N - n) : 8;
+  const bool vec = (N & 7) == 0;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const float *src = part + ((int64_t)s * M + m) * N + n;
+    if (vec) {
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += a[e];
+        acc[4 + e] += b[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < cnt) acc[e] += src[e];
+    }
+  }
+  uint16_t out[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t nn = n + (e < cnt ? e : 0);
+    const float b = bias ? bf16_to_f32(bias[nn]) : 0.0f;
+    out[e] = f32_to_bf16_rne(scale[nn] * acc[e] + b);
+  }
+  uint16_t *dst = y + m * N + n;
+  if (vec) {
+    *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(out);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < cnt) dst[e] = out[e];
+  }
+}
+
 template <int SG>
 hipError_t launch_wide(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
                        const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
   using L = WideLds<SG>;
   static bool attr_set = false;
   if (!attr_set) {  // more than 64 KB of dynamic LDS; a launch the limit refuses reports itself
-    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide<SG>,
+    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide<SG, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     (void)hipGetLastError();
     attr_set = true;
   }
   const int tiles_m = (int)((M + L::BM - 1) / L::BM), tiles_n = (int)((N + L::BNW - 1) / L::BNW);
-  hipLaunchKernelGGL(k_w8a16_gemm_wide<SG>, dim3((unsigned)(tiles_m * tiles_n)), dim3(512),
-                     L::BYTES, st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n);
+  hipLaunchKernelGGL((k_w8a16_gemm_wide<SG, false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512),
+                     L::BYTES, st, x, q, scale, bias, y, M, N, K, tiles_m, tiles_n, nullptr, 0);
+  return hipGetLastError();
+}
+
+// The wide tile over S splits of K into part (S M N floats), then the sum.
+hipError_t launch_wide_split(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
+                             const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
+                             float *part, int S, hipStream_t st) {
+  constexpr int SG = 4;
+  using L = WideLds<SG>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void *)k_w8a16_gemm_wide<SG, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES_SPLIT);
+    (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int tiles_m = (int)((M + L::BM - 1) / L::BM), tiles_n = (int)((N + L::BNW - 1) / L::BNW);
+  const int nk = (int)((K + BK - 1) / BK);
+  int ks = (nk + S - 1) / S;
+  ks = (ks + SG - 1) / SG * SG;  // whole turns of the ring
+  const int splits = (nk + ks - 1) / ks;
+  hipLaunchKernelGGL((k_w8a16_gemm_wide<SG, true>), dim3((unsigned)(tiles_m * tiles_n * splits)),
+                     dim3(512), L::BYTES_SPLIT, st, x, q, scale, bias, y, M, N, K, tiles_m,
+                     tiles_n, part, ks);
+  const int64_t groups = M * ((N + 7) / 8);
+  hipLaunchKernelGGL(k_w8a16_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     st, part, splits, M, N, scale, bias, y);
   return hipGetLastError();
 }
 
@@ -588,14 +709,33 @@ hipError_t launch_wm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, c
 
 }  // namespace
 
-// 128 x 256 tiles from 160 of them on (fewer than one per CU still beats the
-// smaller tiles' extra round), two workgroups a CU from 512 on; else 128 x 128
-// tiles when those fill the CUs, else 64 x 128 tiles with two stage groups
-// and an 8-stage ring (measured at M = 512, K = 14336, N = 4096: 74 us against
-// 95 us for one group of 4 waves).
+int w8a16_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t twide = ((M + 127) / 128) * ((N + 255) / 256);
+  const int64_t nk = (K + BK - 1) / BK;
+  if (twide >= 160 || nk < 128) return 1;
+  int S = 1;
+  while (S < 16 && twide * 2 * S <= 256 && nk / (2 * S) >= 16) S *= 2;
+  return S;
+}
+
+size_t w8a16_gemm_part_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = w8a16_gemm_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * 4 : 0;
+}
+
+// Few wide tiles and long rows (a workspace given): the wide tile over K
+// splits, then the sum (M = 512, N = 4096, K = 14336: 76 vs 89 us; M = 128:
+// 37 vs 82 us; rotated weights). Else 128 x 256 tiles from 160 of them on
+// (fewer than one per CU still beats the smaller tiles' extra round), two
+// workgroups a CU from 512 on; else 128 x 128 tiles when those fill the CUs,
+// else 64 x 128 tiles with two stage groups and an 8-stage ring (measured at
+// M = 512, K = 14336, N = 4096: 74 us against 95 us for one group of 4 waves).
 hipError_t launch_w8a16_gemm(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                              const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
-                             hipStream_t st) {
+                             float *part, size_t part_bytes, hipStream_t st) {
+  const int S = w8a16_gemm_splits(M, N, K);
+  if (S > 1 && part && part_bytes >= w8a16_gemm_part_bytes(M, N, K))
+    return launch_wide_split(x, M, K, q, scale, bias, N, y, part, S, st);
   const int64_t twide = ((M + 127) / 128) * ((N + 255) / 256);
   if (twide >= 512) return launch_wide<2>(x, M, K, q, scale, bias, N, y, st);
   if (twide >= 160) return launch_wide<4>(x, M, K, q, scale, bias, N, y, st);

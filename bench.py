@@ -338,12 +338,14 @@ def sec_llm7b(torch, aql, workloads, dev):
         for M in (1, 4, 16, 512, 2048):
             x = workloads.llm7b(K, 16, M, seed=3)["x"].to(dev)
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-            fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y)
+            nws = aql.aql_workspace_bytes(aql.AQL_OP_W8A16, M, N, K)
+            wsb = torch.empty(nws, dtype=torch.uint8, device=dev) if nws > 0 else None
+            fn = lambda i: aql.aql_linear_w8a16(x, qs[i], s, None, y, workspace=wsb)
             for i in range(ncopy):
                 fn(i)
             if M <= 16:  # short calls: the C entry point with prebuilt arguments
                 fn = raw_call(aql, torch, "aql_linear_w8a16",
-                              [(x, M, K, qs[i], s, None, N, y) for i in range(ncopy)])
+                              [(x, M, K, qs[i], s, None, N, y, None, 0) for i in range(ncopy)])
             med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy,
                                    warm_ms=0.0 if M <= 16 else 40.0)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N

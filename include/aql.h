@@ -71,6 +71,7 @@ extern "C" {
 #define AQL_OP_Q8TA_Q8CSW 1 /* workspace of aql_linear_q8ta_q8csw */
 #define AQL_OP_DQ8CA 2      /* workspace of aql_linear_dq8ca */
 #define AQL_OP_GPTQ_INT8 3  /* workspace of aql_gptq_int8 (M = the column block) */
+#define AQL_OP_W8A16 4      /* optional workspace of aql_linear_w8a16 (0: none used) */
 
 /* Largest K accepted by the int8 paths: keeps |sum_k (xq - z) q| below 2^31. */
 #define AQL_MAX_K_INT8 65536
@@ -188,12 +189,18 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
  *   scale  device, [N] float32
  *   bias   device, [N] bf16 (may be NULL)
  *   y      device, [M, N] bf16, fp32 accumulate, round-to-nearest-even (output)
+ *   ws     device workspace (may be NULL). With at least
+ *          aql_workspace_bytes(AQL_OP_W8A16, M, N, K) bytes (nonzero only for
+ *          prefill shapes of few output tiles and long rows), the tiled kernel
+ *          splits K over more workgroups and adds their fp32 partial sums in a
+ *          second launch; otherwise, or with a smaller workspace, it does not.
+ *          The result is the same up to the order of the fp32 additions.
  * Errors: NULL x/q/scale/y (M, N > 0); M, N < 0; K < 16 or K % 16 != 0;
- * misaligned pointers.
+ * misaligned pointers (ws included).
  */
 int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                      const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
-                     void *stream);
+                     void *ws, size_t ws_bytes, void *stream);
 
 /*
  * W8A8 linear with a static per-tensor affine activation scale and an

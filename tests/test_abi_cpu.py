@@ -99,14 +99,30 @@ def test_act_quant_validation():
 
 def test_w8a16_validation():
     f = L.aql_linear_w8a16
-    assert f(NUL, 1, 64, B, Y, None, 8, Y, None) == aql.AQL_ERR_NULL
-    assert f(A, 1, 64, B, Y, None, 8, NUL, None) == aql.AQL_ERR_NULL
-    assert f(A, 1, 40, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
-    assert f(A, 1, 0, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
-    assert f(A, -1, 64, B, Y, None, 8, Y, None) == aql.AQL_ERR_SHAPE
-    assert f(A, 1, 64, B, Y, MIS, 8, Y, None) == aql.AQL_ERR_ALIGN
-    assert f(A, 0, 64, B, Y, None, 8, Y, None) == aql.AQL_OK
-    assert f(A, 3, 64, B, Y, None, 0, Y, None) == aql.AQL_OK
+    assert f(NUL, 1, 64, B, Y, None, 8, Y, None, 0, None) == aql.AQL_ERR_NULL
+    assert f(A, 1, 64, B, Y, None, 8, NUL, None, 0, None) == aql.AQL_ERR_NULL
+    assert f(A, 1, 40, B, Y, None, 8, Y, None, 0, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 1, 0, B, Y, None, 8, Y, None, 0, None) == aql.AQL_ERR_SHAPE
+    assert f(A, -1, 64, B, Y, None, 8, Y, None, 0, None) == aql.AQL_ERR_SHAPE
+    assert f(A, 1, 64, B, Y, MIS, 8, Y, None, 0, None) == aql.AQL_ERR_ALIGN
+    assert f(A, 1, 64, B, Y, None, 8, Y, MIS, 64, None) == aql.AQL_ERR_ALIGN
+    assert f(A, 0, 64, B, Y, None, 8, Y, None, 0, None) == aql.AQL_OK
+    assert f(A, 3, 64, B, Y, None, 0, Y, None, 0, None) == aql.AQL_OK
+
+
+def test_w8a16_workspace_bytes():
+    """The optional split-K workspace: S x M x N floats for prefill shapes of
+    few 128 x 256 tiles and K >= 8192 (S doubles while the units stay <= 256
+    and each keeps >= 16 stages of 64 k), 0 elsewhere."""
+    wb = lambda M, N, K: L.aql_workspace_bytes(aql.AQL_OP_W8A16, M, N, K)
+    assert wb(512, 4096, 14336) == 4 * 512 * 4096 * 4    # 64 tiles -> 4 splits
+    assert wb(1024, 4096, 14336) == 2 * 1024 * 4096 * 4  # 128 tiles -> 2
+    assert wb(128, 4096, 14336) == 8 * 128 * 4096 * 4    # 16 tiles, 224 stages -> 8
+    assert wb(64, 300, 16384) == 16 * 64 * 300 * 4
+    assert wb(2048, 4096, 14336) == 0                    # 256 wide tiles: no split
+    assert wb(512, 14336, 4096) == 0                     # K < 8192
+    assert wb(16, 4096, 14336) == 0                      # decode band
+    assert wb(512, 4096, -1) == 0
 
 
 def test_q8ta_validation():

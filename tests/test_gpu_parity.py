@@ -312,13 +312,35 @@ def test_w8a16_prefill_shapes(M, N, K, with_bias):
     check_float(y, yref, tol, BF16, f"w8a16 prefill {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(200, 1000, 8208), (64, 300, 16384), (513, 130, 12304)])
+def test_w8a16_prefill_split_k(M, N, K):
+    """Few wide tiles and long rows: with a workspace the wide tile splits K
+    (7, 16 and 8 splits here; ragged M, N and a partial last stage) and a
+    second launch adds the partial sums; with a workspace below the size asked
+    for, the same call runs unsplit. Both against the oracle."""
+    say("w8a16 split-K", M, N, K)
+    nb = aql.aql_workspace_bytes(aql.AQL_OP_W8A16, M, N, K)
+    assert nb > 0
+    g = workloads.gen(750 + M + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+    b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16)
+    q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+    yref, tol = oracle.linear_w8a16(bits(x), host(q), host(s), bits(b))
+    for nbytes in (nb, 16):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        y = aql.aql_linear_w8a16(dev(x), q, s, dev(b), workspace=ws)
+        check_float(host(y.float()), yref, tol, BF16, f"w8a16 split-K {M}x{N}x{K} ws={nbytes}")
+
+
 @pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
 @pytest.mark.parametrize("M", [512, 2048])
 def test_w8a16_llm7b_prefill_full_size(K, N, M):
     """7B shapes at M = 512 and 2048 (the tiled GEMM at its real sizes, both
-    tile shapes), checked on every channel of one random row from each 64-row
-    band (so every 64- and 128-row tile is visited), plus the first and last
-    rows."""
+    tile shapes; M = 512, K = 14336 splits K over 4 workgroups, the binding
+    allocating the workspace), checked on every channel of one random row from
+    each 64-row band (so every 64- and 128-row tile is visited), plus the
+    first and last rows."""
     say("w8a16 7b prefill", K, N, M)
     d = workloads.llm7b(K, N, M, seed=6)
     q, s, _ = aql.aql_quantize_weight_int8(dev(d["w"]), aql.AQL_WQ_SYM127)

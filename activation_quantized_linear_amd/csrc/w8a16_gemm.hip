@@ -493,7 +493,7 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
   for (int s = 0; s < SG - 1; ++s) issue(k0 + s);
   int kt = k0;
   auto step = [&](int k) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (SG - 2)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (SG - 2)));
     __builtin_amdgcn_s_barrier();  // stage k complete everywhere; slot of k-1 free
     issue(k + SG - 1);
     compute(k);
@@ -513,8 +513,8 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
 #pragma unroll
   for (int t = 0; t < SG - 1; ++t) {
     if (kt < nk) {
-      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (SG - 2)));
-      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (SG > 3 ? NL * (SG - 3) : 0));
+      if (t == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (SG - 2)));
+      else if (t == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(SG > 3 ? NL * (SG - 3) : 0));
       else __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       compute(kt);
@@ -590,50 +590,44 @@ __global__ __launch_bounds__(512, SG == 2 ? 4 : 2) void k_w8a16_gemm_wide(const 
 }
 
 // y[m, n] = bf16(scale[n] (part[0][m][n] + ... + part[S-1][m][n]) + bias[n]),
-// the sum in split order; a thread takes 8 consecutive outputs of a row.
+// the sum in split order; a thread takes 4 consecutive outputs of a row (one
+// 16-byte load per split: 4.4 us for S = 4 at M = 512, N = 4096, against 9.5
+// with 8 outputs a thread).
 __global__ __launch_bounds__(256) void k_w8a16_splitk_reduce(const float *__restrict__ part, int S,
                                                             int64_t M, int64_t N,
                                                             const float *__restrict__ scale,
                                                             const uint16_t *__restrict__ bias,
                                                             uint16_t *__restrict__ y) {
-  const int64_t ng = (N + 7) / 8;
+  const int64_t ng = (N + 3) / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= M * ng) return;
-  const int64_t m = i / ng, n = (i % ng) * 8;
-  const int cnt = N - n < 8 ? (int)(N - n) : 8;
-  const bool vec = (N & 7) == 0;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  const int64_t m = i / ng, n = (i % ng) * 4;
+  const int cnt = N - n < 4 ? (int)(N - n) : 4;
+  const bool vec = (N & 3) == 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < S; ++s) {
     const float *src = part + ((int64_t)s * M + m) * N + n;
     if (vec) {
-      const f32x4 a = *reinterpret_cast<const f32x4 *>(src);
-      const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += a[e];
-        acc[4 + e] += b[e];
-      }
+      acc += *reinterpret_cast<const f32x4 *>(src);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 4; ++e)
         if (e < cnt) acc[e] += src[e];
     }
   }
-  uint16_t out[8];
+  uint16_t out[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 4; ++e) {
     const int64_t nn = n + (e < cnt ? e : 0);
     const float b = bias ? bf16_to_f32(bias[nn]) : 0.0f;
     out[e] = f32_to_bf16_rne(scale[nn] * acc[e] + b);
   }
   uint16_t *dst = y + m * N + n;
   if (vec) {
-    *reinterpret_cast<i32x4 *>(dst) = *reinterpret_cast<const i32x4 *>(out);
+    *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(out);
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 4; ++e)
       if (e < cnt) dst[e] = out[e];
   }
 }
@@ -676,7 +670,7 @@ hipError_t launch_wide_split(const uint16_t *x, int64_t M, int64_t K, const int8
   hipLaunchKernelGGL((k_w8a16_gemm_wide<SG, true>), dim3((unsigned)(tiles_m * tiles_n * splits)),
                      dim3(512), L::BYTES_SPLIT, st, x, q, scale, bias, y, M, N, K, tiles_m,
                      tiles_n, part, ks);
-  const int64_t groups = M * ((N + 7) / 8);
+  const int64_t groups = M * ((N + 3) / 4);
   hipLaunchKernelGGL(k_w8a16_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
                      st, part, splits, M, N, scale, bias, y);
   return hipGetLastError();

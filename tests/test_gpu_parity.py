@@ -227,7 +227,8 @@ def test_w8a16_tiny():
                                    (1, 4100, 12288), (1, 9, 2048), (1, 8, 4096), (1, 17, 2064),
                                    (1, 3, 8192), (1, 5, 6160), (1, 13, 65536),
                                    (1, 2049, 4080), (2, 9, 2048), (4, 17, 16384), (3, 1000, 6160),
-                                   (4, 8, 4096), (2, 4100, 14336), (3, 7, 16400)])
+                                   (4, 8, 4096), (2, 4100, 14336), (3, 7, 16400), (3, 14336, 2048),
+                                   (3, 1000, 4096), (4, 3000, 2048)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_w8a16_shapes(M, N, K, with_bias):
     """Ragged W8A16 shapes for every M band. M = 1 with 2048 <= K <= 8192 runs

@@ -255,6 +255,46 @@ __global__ __launch_bounds__(256) void k_quantize_act_per_tensor(
 }
 
 // ------------------------------------------------------------ per-row qparams
+// The min and the max over the TPR threads that own a row, both at once (both
+// are exact in any order): within a wave by DPP moves over lane bits 0-3 and
+// lane-half swaps over bits 4 and 5, across the row's waves through LDS with a
+// single barrier.
+template <int CTRL>
+__device__ __forceinline__ float qp_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int TPR>
+__device__ __forceinline__ void row_minmax(float &mn, float &mx, float2 *lds) {
+  mn = fminf(mn, qp_dpp<0xB1>(mn));  // quad_perm 1,0,3,2
+  mx = fmaxf(mx, qp_dpp<0xB1>(mx));
+  mn = fminf(mn, qp_dpp<0x4E>(mn));  // quad_perm 2,3,0,1
+  mx = fmaxf(mx, qp_dpp<0x4E>(mx));
+  mn = fminf(mn, qp_dpp<0x124>(mn));  // row_ror:4
+  mx = fmaxf(mx, qp_dpp<0x124>(mx));
+  mn = fminf(mn, qp_dpp<0x128>(mn));  // row_ror:8
+  mx = fmaxf(mx, qp_dpp<0x128>(mx));
+  // each lane gets its own value and its partner's (lane ^ 16, then ^ 32)
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+  b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  if constexpr (TPR > 64) {
+    const int w = (threadIdx.x % TPR) >> 6, base = (threadIdx.x / TPR) * (TPR / 64);
+    if ((threadIdx.x & 63) == 0) lds[base + w] = make_float2(mn, mx);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPR / 64; ++i) {
+      const float2 p = lds[base + i];
+      mn = fminf(mn, p.x);
+      mx = fmaxf(mx, p.y);
+    }
+  }
+}
+
 // ExecuTorch 8da4w choose_qparams_affine, read as the affine min/max rule:
 // mn = min(min x, 0), mx = max(max x, 0), s = max((mx - mn) / 255, eps),
 // zp = clamp(-128 - rint(mn / s)), then xq = clamp(rint(x * (1/s)) + zp).
@@ -262,7 +302,7 @@ template <int TPR, int VPT, int MODE>
 __global__ __launch_bounds__(256) void k_choose_qparams_rows(
     const float *__restrict__ x, int64_t M, int64_t K, float *__restrict__ scale,
     int32_t *__restrict__ zp, void *__restrict__ xq) {
-  __shared__ float red_f[4];
+  __shared__ float2 red_mm[4];
   constexpr int RPW = 256 / TPR;
   const int t = threadIdx.x % TPR;
   const int64_t m = (int64_t)blockIdx.x * RPW + threadIdx.x / TPR;
@@ -290,8 +330,7 @@ __global__ __launch_bounds__(256) void k_choose_qparams_rows(
       mx = fmaxf(mx, fmaxf(fmaxf(u.x, u.y), fmaxf(u.z, u.w)));
     }
   }
-  mn = group_reduce_min<TPR>(mn, red_f);
-  mx = group_reduce_max<TPR>(mx, red_f);
+  row_minmax<TPR>(mn, mx, red_mm);
   const float s = fmaxf((mx - mn) / 255.0f, FLT_EPSILON);
   const float zf = clamp_code(-128.0f - rintf(mn / s), -128.0f, 127.0f);
   if (active && t == 0) {

@@ -410,9 +410,9 @@ struct QT {
   // so that a wave's q-th load is of one kind on every wave (the extra loads
   // fetch rows past the tile: the range check makes them zero, and their LDS
   // rows are never read)
-  static constexpr int QA = (BM * 128 / 1024 + NW - 1) / NW;  // bf16 d: 8 rows x 128 B each
-  static constexpr int QB = (BN * 32 / 1024 + NW - 1) / NW;   // nibbles: 32 rows x 32 B
-  static constexpr int QG = (BN * 16 / 1024 + NW - 1) / NW;   // scales: 64 rows x 16 B
+  static constexpr int QA = ((BM + 7) / 8 + NW - 1) / NW;    // bf16 d: 8 rows x 128 B each
+  static constexpr int QB = ((BN + 31) / 32 + NW - 1) / NW;   // nibbles: 32 rows x 32 B
+  static constexpr int QG = ((BN + 63) / 64 + NW - 1) / NW;   // scales: 64 rows x 16 B
   static constexpr int NL = QA + QB + QG;
   static constexpr int A_BYTES = QA * NW * 1024, B_BYTES = QB * NW * 1024, G_BYTES = QG * NW * 1024;
   static constexpr int B_OFF = A_BYTES, G_OFF = A_BYTES + B_BYTES;
@@ -424,8 +424,12 @@ struct QT {
   static constexpr int EPI = XCH + WM * WN * OUT_WAVE;
   static constexpr int LDS = RING > EPI ? RING : EPI;
 };
+// The smaller tiles split each stage's two groups over two waves and keep 3
+// or 4 stages of 12-16 KB in flight, so three workgroups fit a CU's LDS.
 using QTL = QT<4, 4, 2, 2, 1, 3>;  // 128 x 128, large M
-using QTS = QT<4, 2, 1, 2, 2, 4>;  // 64 x 64, groups split over two waves
+using QTM = QT<4, 2, 1, 2, 2, 3>;  // 64 x 64
+using QTN = QT<2, 3, 2, 1, 2, 3>;  // 64 x 48
+using QTR = QT<1, 3, 2, 1, 2, 4>;  // 32 x 48
 
 __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -592,9 +596,9 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   int kt = 0;
-  static_assert(NL * (STAGES - 2) < 16, "vmcnt immediate");
+  static_assert(NL * (STAGES - 2) < 64, "vmcnt immediate");
   for (; kt < nk - (STAGES - 1); ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (STAGES - 2)));
     __builtin_amdgcn_s_barrier();
     issue(kt + STAGES - 1);
     compute(kt);
@@ -604,9 +608,9 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
   for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {
       // stages issued after stage kt: STAGES - 2 - t
-      if (t == 0) __builtin_amdgcn_s_waitcnt(0x0F70 | (NL * (STAGES - 2)));
-      else if (t == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (STAGES > 3 ? NL * (STAGES - 3) : 0));
-      else if (t == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (STAGES > 4 ? NL * (STAGES - 4) : 0));
+      if (t == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (STAGES - 2)));
+      else if (t == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(STAGES > 3 ? NL * (STAGES - 3) : 0));
+      else if (t == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(STAGES > 4 ? NL * (STAGES - 4) : 0));
       else __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       compute(kt);
@@ -761,12 +765,17 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
-    // 128 x 128 tiles once there are more of them than CUs; else 64 x 64 tiles
-    // with the groups split over two waves (K = 4096, N = 11008: 93 vs 100 us
-    // at M = 512, 344 such tiles; 79 vs 35 us at M = 128)
+    // 128 x 128 tiles once there are more of them than CUs (K = 4096, N =
+    // 11008: 93 vs 100 us for 64 x 64 tiles at M = 512, 344 such tiles);
+    // below that the tile that measured fastest at K = 4096, N = 11008: 32 x 48
+    // up to M = 64 (22.3 vs 29.0 us at M = 32 for 64 x 64 tiles in 4 stages),
+    // 64 x 48 up to M = 160 (32.1 vs 35.0 at M = 128), 64 x 64 above (49.2
+    // vs 62.4 at M = 200, 77.7 vs 94.7 at M = 384: 3 stages, 3 workgroups a CU)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
     if (tl >= 320) launch_tiled<QTL>(a, st);
-    else launch_tiled<QTS>(a, st);
+    else if (a.M <= 64) launch_tiled<QTR>(a, st);
+    else if (a.M <= 160) launch_tiled<QTN>(a, st);
+    else launch_tiled<QTM>(a, st);
   }
   return hipGetLastError();
 }

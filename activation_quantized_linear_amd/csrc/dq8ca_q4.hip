@@ -427,6 +427,7 @@ struct QT {
 // The smaller tiles split each stage's two groups over two waves and keep 3
 // or 4 stages of 12-16 KB in flight, so three workgroups fit a CU's LDS.
 using QTL = QT<4, 4, 2, 2, 1, 3>;  // 128 x 128, large M
+using QTW = QT<4, 3, 2, 2, 1, 2>;  // 128 x 96, 2 stages
 using QTM = QT<4, 2, 1, 2, 2, 3>;  // 64 x 64
 using QTN = QT<2, 3, 2, 1, 2, 3>;  // 64 x 48
 using QTR = QT<1, 3, 2, 1, 2, 4>;  // 32 x 48
@@ -459,8 +460,11 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
   constexpr int TI = C::TI, TJ = C::TJ, KH = C::KH, NL = C::NL, STAGES = C::STAGES;
   const int nt = tiles_m * tiles_n;
   const int lin = blockIdx.x;
-  int tile = lin;
-  if ((nt & 7) == 0) tile = (lin & 7) * (nt >> 3) + (lin >> 3);
+  // Workgroups go to the 8 XCDs round-robin (XCD lin mod 8); XCD x takes the
+  // contiguous tile range of its share (the first nt mod 8 XCDs one extra), so
+  // the row tiles of a column tile run under one L2 and read its weights once.
+  const int xq = nt >> 3, xr = nt & 7, x = lin & 7;
+  const int tile = x * xq + (x < xr ? x : xr) + (lin >> 3);
   const int tn = tile / tiles_m, tm = tile % tiles_m;
   const int64_t n0 = (int64_t)tn * C::BN, m0 = (int64_t)tm * C::BM;
   const int64_t M = p.M, N = p.N, K = p.K, G = K / 32, KB = K / 2;
@@ -765,14 +769,17 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
-    // 128 x 128 tiles once there are more of them than CUs (K = 4096, N =
-    // 11008: 93 vs 100 us for 64 x 64 tiles at M = 512, 344 such tiles);
-    // below that the tile that measured fastest at K = 4096, N = 11008: 32 x 48
+    // 128 x 128 tiles once there are more than 2.5 of them a CU (K = 4096, N
+    // = 11008: 280 us at M = 2048 against 302 for 128 x 96), 128 x 96 in 2
+    // stages from 1.25 a CU (82.6 vs 91.0 us for 128 x 128 at M = 512, 165.8
+    // vs 167.5 at M = 1024); below that the tile that measured fastest at
+    // K = 4096, N = 11008: 32 x 48
     // up to M = 64 (22.3 vs 29.0 us at M = 32 for 64 x 64 tiles in 4 stages),
     // 64 x 48 up to M = 160 (32.1 vs 35.0 at M = 128), 64 x 64 above (49.2
     // vs 62.4 at M = 200, 77.7 vs 94.7 at M = 384: 3 stages, 3 workgroups a CU)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
-    if (tl >= 320) launch_tiled<QTL>(a, st);
+    if (tl >= 640) launch_tiled<QTL>(a, st);
+    else if (tl >= 320) launch_tiled<QTW>(a, st);
     else if (a.M <= 64) launch_tiled<QTR>(a, st);
     else if (a.M <= 160) launch_tiled<QTN>(a, st);
     else launch_tiled<QTM>(a, st);

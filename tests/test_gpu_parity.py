@@ -485,15 +485,15 @@ def test_dq8ca_q4_few_rows(M, N, K, with_bias):
     assert np.array_equal(host(y2), y)
 
 
-@pytest.mark.parametrize("M,N,K", [(2000, 4100, 96), (1000, 4100, 160), (50, 1000, 224),
-                                   (33, 47, 4064), (150, 1001, 160), (65, 11008, 4096),
-                                   (300, 700, 96)])
+@pytest.mark.parametrize("M,N,K", [(2600, 4100, 96), (2000, 4100, 96), (1000, 4100, 160),
+                                   (50, 1000, 224), (33, 47, 4064), (150, 1001, 160),
+                                   (65, 11008, 4096), (300, 700, 96)])
 def test_dq8ca_q4_large_tiles_ragged(M, N, K):
     """Each tile shape of the 4-bit tiled kernel with ragged edges in M and N
     and, for K = 96, 160 and 224, an odd number of groups (the last 64-k stage
-    holds one group): 128 x 128 (2000 x 4100: 528 of them), 64 x 64 in 3
-    stages (1000 x 4100: 264 128-tiles, below the switch; 300 x 700), 32 x 48
-    (M <= 64) and 64 x 48 (M <= 160)."""
+    holds one group): 128 x 128 (2600 x 4100: 693 of them), 128 x 96 (2000 x
+    4100: 528 128-tiles), 64 x 64 in 3 stages (1000 x 4100: 264 128-tiles;
+    300 x 700), 32 x 48 (M <= 64) and 64 x 48 (M <= 160)."""
     say("dq8ca q4 large ragged", M, N, K)
     g = workloads.gen(650)
     x = _edge_rows(workloads.small_matrix(g, M, K))

@@ -18,6 +18,8 @@
 // and folded into the fp32 accumulator with its group scale right away.
 #include <float.h>
 
+#include <type_traits>
+
 #include "dq8ca_q4.h"
 
 namespace aql {
@@ -392,26 +394,33 @@ __global__ __launch_bounds__(64 * W) void k_dq8ca_q4_fm(Q4Args p, int xpitch) {
 // accumulator input of every column tile's MFMA.
 //
 // Tile: WM x WN waves of (16 TI) x (16 TJ) outputs, times KH waves taking
-// alternate groups of each 64-k stage (their sums meet in LDS at the end).
-// Operands go global -> LDS by buffer loads that write LDS (bf16 d rows of
-// 128 B with 16-byte chunks XOR-swizzled by (row / 2) mod 8; nibble rows of
-// 32 B with their two group chunks swapped on odd eighths of rows; 16 bytes of
-// group scales per row, of which the stage uses the first two) into a ring,
+// alternate groups of each stage of GS groups (32 GS k; their sums meet in LDS
+// at the end). Operands go global -> LDS by buffer loads that write LDS (bf16
+// d rows of 64 GS bytes with 16-byte chunks XOR-swizzled by (row / 2) mod 8
+// or, for GS = 4, row mod 16; nibble rows of 16 GS bytes, one 16-byte chunk a
+// group, swizzled by (row / 8) mod 2 or (row / 2) mod 4; 16 bytes of group
+// scales per row, of which the stage uses the first GS) into a ring,
 // with exact vmcnt waits and a fence-free barrier as in the int8 GEMM. Every
 // wave issues the same number of loads per stage; the spare ones zero-fill a
 // scratch slot. The output tile is staged in LDS per wave and written as
 // whole rows.
-template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_>
+template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_, int GS_ = 2>
 struct QT {
   static constexpr int TI = TI_, TJ = TJ_, WM = WM_, WN = WN_, KH = KH_, STAGES = STAGES_;
+  // 32-k groups per stage (2 or 4): a stage holds 64 GS bytes of each bf16 d
+  // row (4 GS chunks of 16 B), 16 GS bytes of each nibble row (GS chunks)
+  // and 4 GS bytes of each row's group scales (a 16-byte load)
+  static constexpr int GS = GS_;
+  static_assert(GS == 2 || GS == 4, "groups per stage");
+  static constexpr int RA = 16 / GS, RB = 64 / GS;  // rows per 1 KB load of d / nibbles
   static constexpr int NW = WM * WN * KH;
   static constexpr int BM = 16 * TI * WM, BN = 16 * TJ * WN;
   // loads per stage of each kind, rounded up to a multiple of the wave count
   // so that a wave's q-th load is of one kind on every wave (the extra loads
   // fetch rows past the tile: the range check makes them zero, and their LDS
   // rows are never read)
-  static constexpr int QA = ((BM + 7) / 8 + NW - 1) / NW;    // bf16 d: 8 rows x 128 B each
-  static constexpr int QB = ((BN + 31) / 32 + NW - 1) / NW;   // nibbles: 32 rows x 32 B
+  static constexpr int QA = ((BM + RA - 1) / RA + NW - 1) / NW;  // bf16 d: RA rows x 64 GS B
+  static constexpr int QB = ((BN + RB - 1) / RB + NW - 1) / NW;  // nibbles: RB rows x 16 GS B
   static constexpr int QG = ((BN + 63) / 64 + NW - 1) / NW;   // scales: 64 rows x 16 B
   static constexpr int NL = QA + QB + QG;
   static constexpr int A_BYTES = QA * NW * 1024, B_BYTES = QB * NW * 1024, G_BYTES = QG * NW * 1024;
@@ -429,8 +438,8 @@ struct QT {
 using QTL = QT<4, 4, 2, 2, 1, 3>;  // 128 x 128, large M
 using QTW = QT<4, 3, 2, 2, 1, 2>;  // 128 x 96, 2 stages
 using QTM = QT<4, 2, 1, 2, 2, 3>;  // 64 x 64
-using QTN = QT<2, 3, 2, 1, 2, 3>;  // 64 x 48
-using QTR = QT<1, 3, 2, 1, 2, 4>;  // 32 x 48
+using QTN = QT<2, 3, 2, 1, 2, 3, 4>;  // 64 x 48, 4 groups a stage
+using QTR = QT<1, 3, 2, 1, 2, 4, 4>;  // 32 x 48, 4 groups a stage
 
 __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -452,10 +461,19 @@ __device__ __forceinline__ bf16x8 nib_bf16x8(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_>
+// XOR swizzles of the 16-byte chunks of a stage's rows in LDS: d rows of
+// 4 GS chunks (conflict-free 16-byte fragment reads over 16 rows), nibble rows
+// of GS chunks
+template <int GS>
+__device__ __forceinline__ int q4_swz_a(int row) { return GS == 2 ? (row >> 1) & 7 : row & 15; }
+template <int GS>
+__device__ __forceinline__ int q4_swz_b(int row) { return GS == 2 ? (row >> 3) & 1 : (row >> 1) & 3; }
+
+template <int TI_, int TJ_, int WM_, int WN_, int KH_, int STAGES_, int GS_>
 __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Args p, int tiles_m,
                                                                             int tiles_n) {
-  using C = QT<TI_, TJ_, WM_, WN_, KH_, STAGES_>;
+  using C = QT<TI_, TJ_, WM_, WN_, KH_, STAGES_, GS_>;
+  constexpr int GS = C::GS, SA = 64 * GS, SB = 16 * GS;  // d and nibble bytes a row per stage
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int TI = C::TI, TJ = C::TJ, KH = C::KH, NL = C::NL, STAGES = C::STAGES;
   const int nt = tiles_m * tiles_n;
@@ -490,49 +508,59 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
   for (int q = 0; q < NL; ++q) {
     if (q < C::QA) {
       const int l = q * C::NW + wave;
-      const int row = 8 * l + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
+      const int row = C::RA * l + lane / (4 * GS), c = (lane % (4 * GS)) ^ q4_swz_a<GS>(row);
       off[q] = (uint32_t)row * (uint32_t)(2 * K) + 16u * c;
       lds_off[q] = (uint32_t)(l * 1024);
-      klim[q] = (int)((2 * K - 16 * c + 127) / 128);
+      klim[q] = (int)((2 * K - 16 * c + SA - 1) / SA);
     } else if (q < C::QA + C::QB) {
       const int l = (q - C::QA) * C::NW + wave;
-      const int row = 32 * l + (lane >> 1), c = (lane & 1) ^ ((row >> 3) & 1);
+      const int row = C::RB * l + lane / GS, c = (lane % GS) ^ q4_swz_b<GS>(row);
       off[q] = (uint32_t)row * (uint32_t)KB + 16u * c;
       lds_off[q] = (uint32_t)(C::B_OFF + l * 1024);
-      klim[q] = (int)((KB - 16 * c + 31) / 32);
+      klim[q] = (int)((KB - 16 * c + SB - 1) / SB);
     } else {
       const int l = (q - C::QA - C::QB) * C::NW + wave;
       const int row = 64 * l + lane;
       off[q] = (uint32_t)row * (uint32_t)(G * 4);
       lds_off[q] = (uint32_t)(C::G_OFF + l * 1024);
-      klim[q] = (int)((G + 1) / 2);
+      klim[q] = (int)((G + GS - 1) / GS);
     }
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  auto issue = [&](int kt) {
+  const int nk = (int)((K + 32 * GS - 1) / (32 * GS));
+  // Before the last stage every lane's bytes lie inside its row: the stage's
+  // offset along the row is uniform and goes in the scalar offset, with no
+  // per-lane range test. The last stage (and any past it) tests each lane.
+  auto issue_as = [&](int kt, auto full) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
-      const uint32_t kstep = q < C::QA ? 128u : (q < C::QA + C::QB ? 32u : 8u);
+      const uint32_t kstep = q < C::QA ? (uint32_t)SA : (q < C::QA + C::QB ? (uint32_t)SB : 4u * GS);
       const uint32_t dst = lds_base + lds_off[q] + (uint32_t)((kt % STAGES) * C::STAGE);
-      const int o = kt < klim[q] ? (int)(off[q] + kstep * (uint32_t)kt) : OOB;
       lds_void *d = (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(dst);
       const __amdgpu_buffer_rsrc_t rs = q < C::QA ? ra : (q < C::QA + C::QB ? rb : rg);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, o, 0, 0, 0);
+      if constexpr (decltype(full)::value) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, (int)off[q], (int)(kstep * (uint32_t)kt), 0, 0);
+      } else {
+        const int o = kt < klim[q] ? (int)(off[q] + kstep * (uint32_t)kt) : OOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, d, 16, o, 0, 0, 0);
+      }
     }
   };
+  auto issue_full = [&](int kt) { issue_as(kt, std::true_type{}); };
+  auto issue_tail = [&](int kt) { issue_as(kt, std::false_type{}); };
 
   f32x4 f[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) f[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int kt) {
+  auto compute = [&](int kt) __attribute__((always_inline)) {
     const char *st = smem + (kt % STAGES) * C::STAGE;
     const bf16x8 bneg = bf16x8_splat(0xC308u);  // -136 in every element
 #pragma unroll
-    for (int x = 0; x < 2 / KH; ++x) {
+    for (int x = 0; x < GS / KH; ++x) {
       const int gg = kh + KH * x;  // group within the stage
-      if (2 * kt + gg < G) {       // uniform: the last stage may hold one group
+      if (GS * kt + gg < (int)G) { // uniform: the last stage may hold fewer groups
         bf16x8 a[TI], b[TJ];
         f32x4 corr[TI];
         float gsv[TJ];
@@ -540,13 +568,13 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
         for (int i = 0; i < TI; ++i) {
           const int R = wm * 16 * TI + 16 * i + r;
           const int c = 4 * gg + g4;
-          a[i] = *reinterpret_cast<const bf16x8 *>(st + R * 128 + 16 * (c ^ ((R >> 1) & 7)));
+          a[i] = *reinterpret_cast<const bf16x8 *>(st + R * SA + 16 * (c ^ q4_swz_a<GS>(R)));
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           const int R = wn * 16 * TJ + 16 * j + r;
           const uint32_t w = *reinterpret_cast<const uint32_t *>(
-              st + C::B_OFF + R * 32 + 16 * (gg ^ ((R >> 3) & 1)) + 4 * g4);
+              st + C::B_OFF + R * SB + 16 * (gg ^ q4_swz_b<GS>(R)) + 4 * g4);
           b[j] = nib_bf16x8(w);
           gsv[j] = *reinterpret_cast<const float *>(st + C::G_OFF + R * 16 + 4 * gg);
         }
@@ -596,17 +624,30 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
     }
   };
 
-  const int nk = (int)((K + 63) / 64);
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if (s < nk - 1) issue_full(s);
+    else issue_tail(s);
+  }
   int kt = 0;
   static_assert(NL * (STAGES - 2) < 64, "vmcnt immediate");
-  for (; kt < nk - (STAGES - 1); ++kt) {
+  auto step = [&](int k, auto full) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NL * (STAGES - 2)));
     __builtin_amdgcn_s_barrier();
-    issue(kt + STAGES - 1);
-    compute(kt);
+    issue_as(k + STAGES - 1, full);
+    compute(k);
     __builtin_amdgcn_s_waitcnt(0xC07F);
+  };
+  // stages whose issue is full (up to nk - 2): whole turns of the ring first,
+  // so that each step's LDS slot offsets are constants
+  for (; kt + STAGES <= nk - STAGES; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) step(kt + u, std::true_type{});
+  }
+  for (; kt < nk - STAGES; ++kt) step(kt, std::true_type{});
+  if (kt < nk - (STAGES - 1)) {                                 // issues the last stage
+    step(kt, std::false_type{});
+    ++kt;
   }
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) {
@@ -715,7 +756,7 @@ void launch_stream_tg(int MB, int W, dim3 grid, const Q4Args &a, hipStream_t st)
 
 template <typename C>
 void launch_tiled(const Q4Args &a, hipStream_t st) {
-  constexpr auto kern = k_dq8ca_q4_tiled<C::TI, C::TJ, C::WM, C::WN, C::KH, C::STAGES>;
+  constexpr auto kern = k_dq8ca_q4_tiled<C::TI, C::TJ, C::WM, C::WN, C::KH, C::STAGES, C::GS>;
   const int tiles_m = (int)((a.M + C::BM - 1) / C::BM);
   const int tiles_n = (int)((a.N + C::BN - 1) / C::BN);
   // more than 64 KB of dynamic LDS: raise the function's limit once (a launch

@@ -528,9 +528,10 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
   const int nk = (int)((K + 32 * GS - 1) / (32 * GS));
-  // Before the last stage every lane's bytes lie inside its row: the stage's
-  // offset along the row is uniform and goes in the scalar offset, with no
-  // per-lane range test. The last stage (and any past it) tests each lane.
+  // The first nf stages lie inside every row for every load (d and nibbles up
+  // to the last stage; the 16-byte group-scale load up to stage (G - 4) / GS):
+  // their offset along the row is uniform and goes in the scalar offset, with
+  // no per-lane range test. Later stages test each lane.
   auto issue_as = [&](int kt, auto full) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NL; ++q) {
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
       }
     }
   };
+  const int nf = G >= 4 ? min(nk - 1, (int)(G - 4) / GS + 1) : 0;
   auto issue_full = [&](int kt) { issue_as(kt, std::true_type{}); };
   auto issue_tail = [&](int kt) { issue_as(kt, std::false_type{}); };
 
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
-    if (s < nk - 1) issue_full(s);
+    if (s < nf) issue_full(s);
     else issue_tail(s);
   }
   int kt = 0;
@@ -638,17 +640,14 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
     compute(k);
     __builtin_amdgcn_s_waitcnt(0xC07F);
   };
-  // stages whose issue is full (up to nk - 2): whole turns of the ring first,
-  // so that each step's LDS slot offsets are constants
-  for (; kt + STAGES <= nk - STAGES; kt += STAGES) {
+  // steps issuing stages below nf: whole turns of the ring first, so that
+  // each step's LDS slot offsets are constants
+  for (; kt + 2 * STAGES - 1 <= nf; kt += STAGES) {
 #pragma unroll
     for (int u = 0; u < STAGES; ++u) step(kt + u, std::true_type{});
   }
-  for (; kt < nk - STAGES; ++kt) step(kt, std::true_type{});
-  if (kt < nk - (STAGES - 1)) {                                 // issues the last stage
-    step(kt, std::false_type{});
-    ++kt;
-  }
+  for (; kt + STAGES - 1 < nf; ++kt) step(kt, std::true_type{});
+  for (; kt < nk - (STAGES - 1); ++kt) step(kt, std::false_type{});
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t) {
     if (kt < nk) {

@@ -429,17 +429,19 @@ struct QT {
   static constexpr int RING = STAGES * STAGE;
   static constexpr int OUT_LD = 16 * TJ + 4;  // words per staged output row
   static constexpr int OUT_WAVE = 16 * TI * OUT_LD * 4;
-  static constexpr int XCH = KH == 2 ? WM * WN * 64 * TI * TJ * 16 : 0;  // partial sums of kh = 1
+  static_assert((KH == 1 || KH == 2 || KH == 4) && GS % KH == 0, "group split");
+  static constexpr int XCH = (KH - 1) * WM * WN * 64 * TI * TJ * 16;  // partial sums of kh > 0
   static constexpr int EPI = XCH + WM * WN * OUT_WAVE;
   static constexpr int LDS = RING > EPI ? RING : EPI;
 };
-// The smaller tiles split each stage's two groups over two waves and keep 3
-// or 4 stages of 12-16 KB in flight, so three workgroups fit a CU's LDS.
-using QTL = QT<4, 4, 2, 2, 1, 3>;  // 128 x 128, large M
-using QTW = QT<4, 3, 2, 2, 1, 2>;  // 128 x 96, 2 stages
-using QTM = QT<4, 2, 1, 2, 2, 3>;  // 64 x 64
-using QTN = QT<2, 3, 2, 1, 2, 3, 4>;  // 64 x 48, 4 groups a stage
-using QTR = QT<1, 3, 2, 1, 2, 4, 4>;  // 32 x 48, 4 groups a stage
+// The smaller tiles take stages of 4 groups, one group to each of 4 waves
+// that all cover the whole tile (its nibbles are unpacked once per group), and
+// keep 3 stages in flight.
+using QTL = QT<4, 4, 2, 2, 1, 3>;     // 128 x 128, large M
+using QTW = QT<4, 3, 2, 2, 1, 2>;     // 128 x 96, 2 stages
+using QTM = QT<4, 4, 1, 1, 4, 3, 4>;  // 64 x 64
+using QTN = QT<2, 3, 1, 2, 4, 3, 4>;  // 32 x 96
+using QTR = QT<2, 3, 1, 1, 4, 3, 4>;  // 32 x 48
 
 __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -665,22 +667,26 @@ __global__ __launch_bounds__(64 * WM_ * WN_ * KH_, 2) void k_dq8ca_q4_tiled(Q4Ar
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();  // ring no longer read or written
 
-  // ---- KH = 2: waves kh = 1 hand their sums to kh = 0
+  // ---- KH > 1: waves kh > 0 hand their sums to kh = 0, which adds them in
+  // the order of kh
   const int pw = wm * C::WN + wn;  // plane wave 0 .. WM WN - 1
-  if constexpr (KH == 2) {
+  if constexpr (KH > 1) {
     f32x4 *xch = reinterpret_cast<f32x4 *>(smem);
-    if (kh == 1) {
+    constexpr int PLANE = C::WM * C::WN * TI * TJ * 64;  // f32x4 per kh slot
+    if (kh > 0) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) xch[((pw * TI + i) * TJ + j) * 64 + lane] = f[i][j];
+        for (int j = 0; j < TJ; ++j) xch[(kh - 1) * PLANE + ((pw * TI + i) * TJ + j) * 64 + lane] = f[i][j];
     }
     __syncthreads();
     if (kh == 0) {
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+      for (int h = 1; h < KH; ++h)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) f[i][j] += xch[((pw * TI + i) * TJ + j) * 64 + lane];
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) f[i][j] += xch[(h - 1) * PLANE + ((pw * TI + i) * TJ + j) * 64 + lane];
     }
   }
   if (kh != 0) return;
@@ -809,19 +815,19 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     if (TG == 2) launch_stream_tg<2>(MB, W, grid, a, st);
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
-    // 128 x 128 tiles once there are more than 2.5 of them a CU (K = 4096, N
-    // = 11008: 280 us at M = 2048 against 302 for 128 x 96), 128 x 96 in 2
-    // stages from 1.25 a CU (82.6 vs 91.0 us for 128 x 128 at M = 512, 165.8
-    // vs 167.5 at M = 1024); below that the tile that measured fastest at
-    // K = 4096, N = 11008: 32 x 48
-    // up to M = 64 (22.3 vs 29.0 us at M = 32 for 64 x 64 tiles in 4 stages),
-    // 64 x 48 up to M = 160 (32.1 vs 35.0 at M = 128), 64 x 64 above (49.2
-    // vs 62.4 at M = 200, 77.7 vs 94.7 at M = 384: 3 stages, 3 workgroups a CU)
+    // Tile by the rows and the count of 128 x 128 tiles, as measured at
+    // K = 4096, N = 11008: 128 x 128 from 2.5 such tiles a CU (277 us at
+    // M = 2048 against 294 for 128 x 96), 128 x 96 in 2 stages from M = 384
+    // (68.9 vs 78.0 us for 64 x 64 at M = 384, 75.3 vs 84.2 for 128 x 128 at
+    // M = 512); below that 32 x 48 up to M = 64 (14.9 us at M = 32, 25.7 for
+    // 64 x 64 tiles with two groups a stage over two waves), 32 x 96 up to
+    // M = 256 (27.9 vs 31.8 at M = 128) and 64 x 64 above (56.0 vs 62.3 at
+    // M = 300)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
     if (tl >= 640) launch_tiled<QTL>(a, st);
-    else if (tl >= 320) launch_tiled<QTW>(a, st);
+    else if (a.M >= 384) launch_tiled<QTW>(a, st);
     else if (a.M <= 64) launch_tiled<QTR>(a, st);
-    else if (a.M <= 160) launch_tiled<QTN>(a, st);
+    else if (a.M <= 256) launch_tiled<QTN>(a, st);
     else launch_tiled<QTM>(a, st);
   }
   return hipGetLastError();

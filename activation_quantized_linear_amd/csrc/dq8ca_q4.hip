@@ -440,7 +440,8 @@ struct QT {
 using QTL = QT<4, 4, 2, 2, 1, 3>;     // 128 x 128, large M
 using QTW = QT<4, 3, 2, 2, 1, 2>;     // 128 x 96, 2 stages
 using QTM = QT<4, 4, 1, 1, 4, 3, 4>;  // 64 x 64
-using QTN = QT<2, 3, 1, 2, 4, 3, 4>;  // 32 x 96
+using QTN = QT<4, 3, 1, 1, 4, 3, 4>;  // 64 x 48
+using QTP = QT<2, 3, 1, 2, 4, 3, 4>;  // 32 x 96
 using QTR = QT<2, 3, 1, 1, 4, 3, 4>;  // 32 x 48
 
 __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
@@ -816,17 +817,19 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     else launch_stream_tg<4>(MB, W, grid, a, st);
   } else {
     // Tile by the rows and the count of 128 x 128 tiles, as measured at
-    // K = 4096, N = 11008: 128 x 128 from 2.5 such tiles a CU (277 us at
-    // M = 2048 against 294 for 128 x 96), 128 x 96 in 2 stages from M = 384
-    // (68.9 vs 78.0 us for 64 x 64 at M = 384, 75.3 vs 84.2 for 128 x 128 at
-    // M = 512); below that 32 x 48 up to M = 64 (14.9 us at M = 32, 25.7 for
-    // 64 x 64 tiles with two groups a stage over two waves), 32 x 96 up to
-    // M = 256 (27.9 vs 31.8 at M = 128) and 64 x 64 above (56.0 vs 62.3 at
-    // M = 300)
+    // K = 4096, N = 11008 with the weights streamed from HBM: 128 x 128 from
+    // 2.5 such tiles a CU (277 us at M = 2048 against 294 for 128 x 96),
+    // 128 x 96 in 2 stages from M = 384 (70.4 vs 74.9 us for 64 x 48 at
+    // M = 384, 75.3 vs 84.2 for 128 x 128 at M = 512); below that 32 x 48 up
+    // to M = 32 (15.7 us, 26.0 for 64 x 64 tiles with two groups a stage over
+    // two waves), 32 x 96 up to M = 64 (19.6 vs 20.9 for 32 x 48), 64 x 48 up
+    // to M = 256 (29.7 vs 37.8 at M = 128, 47.1 vs 56.6 at M = 200) and
+    // 64 x 64 above (58.2 vs 67.8 at M = 300)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
     if (tl >= 640) launch_tiled<QTL>(a, st);
     else if (a.M >= 384) launch_tiled<QTW>(a, st);
-    else if (a.M <= 64) launch_tiled<QTR>(a, st);
+    else if (a.M <= 32) launch_tiled<QTR>(a, st);
+    else if (a.M <= 64) launch_tiled<QTP>(a, st);
     else if (a.M <= 256) launch_tiled<QTN>(a, st);
     else launch_tiled<QTM>(a, st);
   }

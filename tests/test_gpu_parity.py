@@ -486,14 +486,14 @@ def test_dq8ca_q4_few_rows(M, N, K, with_bias):
 
 
 @pytest.mark.parametrize("M,N,K", [(2600, 4100, 96), (2000, 4100, 96), (1000, 4100, 160),
-                                   (50, 1000, 224), (33, 47, 4064), (150, 1001, 160),
-                                   (65, 11008, 4096), (300, 700, 96)])
+                                   (50, 1000, 224), (33, 47, 4064), (30, 201, 4064),
+                                   (150, 1001, 160), (65, 11008, 4096), (300, 700, 96)])
 def test_dq8ca_q4_large_tiles_ragged(M, N, K):
     """Each tile shape of the 4-bit tiled kernel with ragged edges in M and N
     and group counts that leave the last stage partly empty (K = 96, 160, 224
     and 4064): 128 x 128 (2600 x 4100: 693 of them), 128 x 96 (2000 x 4100,
-    1000 x 4100), 64 x 64 with the groups over 4 waves (300 x 700), 32 x 96
-    (65 < M <= 256) and 32 x 48 (M <= 64)."""
+    1000 x 4100), and with the groups over 4 waves 64 x 64 (300 x 700), 64 x 48
+    (65 <= M <= 256), 32 x 96 (33 <= M <= 64) and 32 x 48 (M <= 32)."""
     say("dq8ca q4 large ragged", M, N, K)
     g = workloads.gen(650)
     x = _edge_rows(workloads.small_matrix(g, M, K))

@@ -45,6 +45,9 @@ struct W8A16Shape {
 W8A16Shape w8a16_shape(int64_t M, int64_t N, int64_t K);
 constexpr int kW8A16Skinny = 16;     // mblocks value of the skinny tile
 constexpr int kW8A16SkinnyMinM = 4;  // rows from which the skinny tile serves (up to the GEMM band)
+// From this many channels launch_w8a16 runs the skinny tile's shared-x form
+// (64 channels a workgroup, x copied into LDS once per step for 4 waves).
+constexpr int64_t kW8A16ShareMinN = 8192;
 // LDS budget for x in the single-row tile (K <= 16384), and the xlds value for
 // a given K (0 past the budget).
 constexpr int kW8A16MaxXlds = 32768;

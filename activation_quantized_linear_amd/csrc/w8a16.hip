@@ -996,6 +996,142 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_sk_grouped(const W8A16GroupEnt
   w8a16_tile_sk<W, NT>(group_tile(tab, count, 16 * NT), sm);
 }
 
+// Skinny tile with x shared through LDS (row blocks of 16, N >= kW8A16ShareMinN).
+// The WC waves of one of the workgroup's WK K ranges take 16 channels each over
+// the same steps, so a 256-k step of x (16 rows x 512 B) comes from L2 once per
+// WC waves instead of once per wave (with 16-channel tiles the x reads of the
+// skinny tile above are twice its weight bytes). Each wave of a range copies
+// 8 / WC of the step's 1 KB pieces into the range's LDS slot by buffer loads
+// that write LDS, row r's 16-byte chunk c at slot c ^ r (16 rows' chunk c then
+// lie in 16 distinct bank groups); the waves meet at a workgroup barrier once
+// the step has landed and again before its slot is refilled. Weights arrive as
+// in the skinny tile (4 rows x 256 B per load into per-wave slots), and the k
+// order within a step is the same. The K ranges' sums meet in LDS.
+template <int WC, int WK>
+struct ShLds {
+  uint8_t w[WC * WK][2][16 * 256];  // per wave, two step slots of 16 rows x 256 B
+  uint8_t x[WK][2][16 * 512];       // per K range, two step slots of 16 rows x 512 B
+  f32x4 red[WC * WK][64];
+};
+
+template <int WC, int WK>
+__global__ __launch_bounds__(64 * WC * WK) void k_w8a16_sksh(const uint16_t *__restrict__ x, int64_t M,
+                                                             int64_t K, const int8_t *__restrict__ q,
+                                                             const float *__restrict__ scale,
+                                                             const uint16_t *__restrict__ bias,
+                                                             int64_t N, uint16_t *__restrict__ y) {
+  static_assert(8 % WC == 0, "x pieces split over a range's waves");
+  __shared__ __attribute__((aligned(16))) ShLds<WC, WK> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wc = wave % WC, wk = wave / WC;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * WC) + 16 * wc;
+  const int64_t m0 = (int64_t)blockIdx.y * 16;
+  const int64_t nrows = N - n0 <= 0 ? 0 : (N - n0 < 16 ? N - n0 : 16);
+  const int64_t mrows = M - m0 < 16 ? M - m0 : 16;
+  const __amdgpu_buffer_rsrc_t rq = rsrc(nrows > 0 ? q + n0 * K : q, (uint32_t)(nrows * K));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, (uint32_t)(mrows * K * 2));
+  const int nst = (int)((K + 255) >> 8);
+  // range wk takes steps wk, wk + WK, ...; every wave runs the same number of
+  // steps (for the barriers), steps past its range load zeros
+  const int cnt = (nst + WK - 1) / WK;
+  const int drow = lane >> 4, dslot = lane & 15;
+  const uint32_t lw0 = (uint32_t)(uintptr_t)&sm.w[wave][0][0];
+  const uint32_t lx0 = (uint32_t)(uintptr_t)&sm.x[wk][0][0];
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int XP = 8 / WC;  // x pieces a wave copies per step
+  constexpr int NV = 4 + XP;  // vector memory instructions per step and wave
+  auto fetch = [&](int i, int slot) {
+    const int st = wk + WK * i;
+    const bool valid = st < nst;  // uniform
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int row = 4 * d + drow;
+      const int c = dslot ^ row;
+      const bool kin = valid && (256 * st + 16 * c) < K;
+      const int qo = kin ? (int)((uint32_t)row * (uint32_t)K + 256u * st + 16u * c) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rq, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(lw0 + (uint32_t)slot * 4096u + 1024u * d),
+          16, qo, 0, 0, 0);
+    }
+    // piece p holds x rows 2 p and 2 p + 1: lane l writes row 2 p + l / 32, slot l % 32
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int p = wc * XP + u;
+      const int row = 2 * p + (lane >> 5), c = (lane & 31) ^ row;
+      const bool kin = valid && row < mrows && (256 * st + 8 * c) < K;
+      const int xo = kin ? (int)((uint32_t)row * (uint32_t)(2 * K) + 512u * st + 16u * c) : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void *)(uintptr_t)__builtin_amdgcn_readfirstlane(lx0 + (uint32_t)slot * 8192u + 1024u * p),
+          16, xo, 0, 0, 0);
+    }
+  };
+  auto mul = [&](int slot) {
+    const uint8_t *wl = &sm.w[wave][slot][0];
+    const uint8_t *xl = &sm.x[wk][slot][0];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const i32x4 wq = *reinterpret_cast<const i32x4 *>(wl + 256 * r + 16 * ((4 * h + g) ^ r));
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        // row r, k = 64 h + 16 g + 8 half .. + 7: x chunk 8 h + 2 g + half
+        const int cx = 8 * h + 2 * g + half;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(xl + 512 * r + 16 * (cx ^ r));
+        const s16x4 lo = widen4(wq[2 * half]), hi = widen4(wq[2 * half + 1]);
+        const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, i32x4{l2[0], l2[1], h2[0], h2[1]});
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  };
+
+  // Step b's loads are out when it starts: wait until only the next step's
+  // remain (this wave's parts of step b have landed), meet the other waves
+  // (theirs too), multiply, then meet again once every wave has read the slot
+  // before it is refilled.
+  fetch(0, 0);
+  for (int b = 0; b < cnt; b += 2) {
+    fetch(b + 1, 1);
+    sk_wait_vm<NV>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mul(0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads done
+    __builtin_amdgcn_s_barrier();
+    fetch(b + 2, 0);
+    sk_wait_vm<NV>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    mul(1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+  }
+  sk_wait_vm<0>();
+
+  // the ranges' sums meet in LDS (added in the order of the range);
+  // lane l of wave (0, wc) holds rows 4 g + v of channel n0 + r
+  if constexpr (WK > 1) {
+    sm.red[wave][lane] = acc;
+    __syncthreads();
+    if (wk != 0) return;
+#pragma unroll
+    for (int k = 1; k < WK; ++k) acc += sm.red[k * WC + wc][lane];
+  }
+  const int64_t n = n0 + r;
+  if (n >= N) return;
+  const float s = scale[n];
+  const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t mm = m0 + 4 * g + v;
+    if (mm < M) y[mm * N + n] = f32_to_bf16_rne(s * acc[v] + bv);
+  }
+}
+
 // Single-row tile; dynamic LDS holds x when XL.
 template <int W, int CW, bool XL>
 __global__ __launch_bounds__(64 * W * CW, 4) void k_w8a16_m1(const uint16_t *__restrict__ x,
@@ -1257,6 +1393,18 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
     return launch_w8a16_m1c(x, K, q, scale, bias, N, y, st);
   if (M >= 2 && M <= kW8A16FewMaxM && K >= kW8A16FewMinK && K <= kW8A16FewMaxK)
     return launch_w8a16_mfew(x, M, K, q, scale, bias, N, y, st);
+  if (M >= kW8A16SkinnyMinM && N >= kW8A16ShareMinN) {
+    // 64 channels a workgroup; one K range for rows of up to 4 KiB once there
+    // are 192 workgroups a row block, else two (M = 16: K = 4096, N = 14336:
+    // 14.2 us against 17.8 for the skinny tile; N = 11008: 13.0 vs 17.0;
+    // K = N = 8192: 20.0 vs 22.4)
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16));
+    if (N >= 12288 && K <= 4096)
+      hipLaunchKernelGGL((k_w8a16_sksh<4, 1>), grid, dim3(256), 0, st, x, M, K, q, scale, bias, N, y);
+    else
+      hipLaunchKernelGGL((k_w8a16_sksh<4, 2>), grid, dim3(512), 0, st, x, M, K, q, scale, bias, N, y);
+    return hipGetLastError();
+  }
   return launch_w8a16_shape(w8a16_shape(M, N, K), x, M, K, q, scale, bias, N, y, st);
 }
 

@@ -63,8 +63,12 @@ __device__ __forceinline__ void wait_vm() {
 // s_waitcnt lgkmcnt(0) (vmcnt / expcnt at their maxima).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int EPI, bool TWO>
+// MODE: 0 one pass, 128 rows a tile; 1 two passes stacked, 64 rows a tile;
+// 2 one pass, 64 rows a tile, in the two-pass layout with the pass-2 half of
+// the A tile zero-filled (for grids that would otherwise leave CUs idle).
+template <int EPI, int MODE>
 __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int tiles_n) {
+  constexpr bool TWO = MODE != 0;  // the two-pass A-tile layout
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int nt = tiles_m * tiles_n;
@@ -91,8 +95,10 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
   const int64_t mval = M - m0 < MROWS ? M - m0 : MROWS;
   const int64_t nval = N - n0 < BN ? N - n0 : BN;
   const bool apass2 = TWO && ((16 * wave) & 63) >= 32;
-  const int8_t *abase = apass2 ? p.a2 : p.a1;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(abase + m0 * K, (uint32_t)(mval * K));
+  const int8_t *abase = apass2 && MODE == 1 ? p.a2 : p.a1;
+  // MODE 2: the pass-2 half of the tile reads nothing (an empty range loads zeros)
+  const __amdgpu_buffer_rsrc_t ra =
+      rsrc(abase + m0 * K, MODE == 2 && apass2 ? 0u : (uint32_t)(mval * K));
   const __amdgpu_buffer_rsrc_t rb = rsrc(p.b + n0 * K, (uint32_t)(nval * K));
   uint32_t aoff[2], boff[2];
   int chunk[2];
@@ -233,7 +239,14 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
         // sum_k (xq - z) q = acc - z * wsum fits int32 (|.| <= K * 255 * 128); the
         // intermediate terms are formed in wrapping unsigned arithmetic.
         const uint32_t zw1 = (uint32_t)p.z1 * (uint32_t)ws, zw2 = (uint32_t)p.z2 * (uint32_t)ws;
-        if constexpr (TWO) {
+        if constexpr (MODE == 2) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              t[(wm * 32 + i * 16 + 4 * g + v) * TILE_LD + col] =
+                  wsc * (p.s1 * (float)(int)((uint32_t)acc[i][j][v] - zw1)) + b;
+        } else if constexpr (TWO) {
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -291,18 +304,18 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
   }
 }
 
-template <int EPI, bool TWO>
+template <int EPI, int MODE>
 hipError_t launch_one(const GemmArgs &a, int tiles_m, int tiles_n, hipStream_t st) {
   // More than 64 KB of dynamic LDS: raise the function's limit once. Its status
   // is not needed: a launch the limit does not allow reports its own error.
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)k_gemm_i8<EPI, TWO>,
+    (void)hipFuncSetAttribute((const void *)k_gemm_i8<EPI, MODE>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     (void)hipGetLastError();
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_gemm_i8<EPI, TWO>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512),
+  hipLaunchKernelGGL((k_gemm_i8<EPI, MODE>), dim3((unsigned)(tiles_m * tiles_n)), dim3(512),
                      LDS_BYTES, st, a, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -310,15 +323,17 @@ hipError_t launch_one(const GemmArgs &a, int tiles_m, int tiles_n, hipStream_t s
 }  // namespace
 
 hipError_t launch_gemm_i8(const GemmArgs &a, GemmEpi epi, bool two_pass, hipStream_t st) {
-  const int rows = two_pass ? BM / 2 : BM;
-  const int tiles_m = (int)((a.M + rows - 1) / rows);
   const int tiles_n = (int)((a.N + BN - 1) / BN);
+  const int tiles_m128 = (int)((a.M + BM - 1) / BM), tiles_m64 = (int)((a.M + BM / 2 - 1) / (BM / 2));
   switch (epi) {
-    case EPI_RAW: return launch_one<EPI_RAW, false>(a, tiles_m, tiles_n, st);
+    case EPI_RAW: return launch_one<EPI_RAW, 0>(a, tiles_m128, tiles_n, st);
     case EPI_Q8TA:
-      return two_pass ? launch_one<EPI_Q8TA, true>(a, tiles_m, tiles_n, st)
-                      : launch_one<EPI_Q8TA, false>(a, tiles_m, tiles_n, st);
-    case EPI_DQ8: return launch_one<EPI_DQ8, false>(a, tiles_m, tiles_n, st);
+      if (two_pass) return launch_one<EPI_Q8TA, 1>(a, tiles_m64, tiles_n, st);
+      // one pass: 64-row tiles while 128-row tiles would leave CUs idle
+      // (M = 512, N = K = 4096: 128 tiles of 128 rows)
+      if (tiles_m128 * tiles_n < 256) return launch_one<EPI_Q8TA, 2>(a, tiles_m64, tiles_n, st);
+      return launch_one<EPI_Q8TA, 0>(a, tiles_m128, tiles_n, st);
+    case EPI_DQ8: return launch_one<EPI_DQ8, 0>(a, tiles_m128, tiles_n, st);
   }
   return hipErrorInvalidValue;
 }

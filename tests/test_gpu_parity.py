@@ -372,12 +372,15 @@ def _calib(x_rows):
     return float(s[0]), int(z[0])
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 200, 256), (130, 129, 272), (64, 128, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 16), (37, 200, 256), (130, 129, 272), (64, 128, 1024),
+                                   (2050, 2100, 64)])
 @pytest.mark.parametrize("two_pass,z2", [(False, 0), (True, 0), (True, -5), (True, 7)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_q8ta_shapes(M, N, K, two_pass, z2, with_bias):
     """Static W8A8 on ragged shapes, one and two passes; the second pass with
-    its own zero point z2 (folded as acc2 - z2 * wsum)."""
+    its own zero point z2 (folded as acc2 - z2 * wsum). One pass takes 64-row
+    tiles while 128-row tiles would be fewer than 256, 128-row tiles from
+    there (2050 x 2100: 17 x 17 of them)."""
     say("q8ta", M, N, K, two_pass, z2, with_bias)
     d = workloads.two_pass(seed=11 + M, M=max(M, 2), K=K, N=N)
     x = d["x"][:M].contiguous()

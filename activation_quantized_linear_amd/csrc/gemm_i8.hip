@@ -225,12 +225,15 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
       const int col = wn * 64 + j * 16 + r;
       const int64_t n = n0 + col;
       const bool nin = n < N;
+      // output rows of this wave: MROWS / 2 from row wm MROWS / 2 (MODE 2: only
+      // the first two MFMA rows of each wave hold pass-1 rows)
+      constexpr int RI = MODE == 2 ? 2 : 4;
       if constexpr (EPI == EPI_RAW) {
         int *t = reinterpret_cast<int *>(tl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RI; ++i)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) t[(wm * 64 + i * 16 + 4 * g + v) * TILE_LD + col] = acc[i][j][v];
+          for (int v = 0; v < 4; ++v) t[(wm * (MROWS / 2) + i * 16 + 4 * g + v) * TILE_LD + col] = acc[i][j][v];
       } else if constexpr (EPI == EPI_Q8TA) {
         float *t = reinterpret_cast<float *>(tl);
         const int ws = nin ? p.wsum[n] : 0;
@@ -269,10 +272,10 @@ __global__ __launch_bounds__(512) void k_gemm_i8(GemmArgs p, int tiles_m, int ti
         const float wsc = nin ? p.wscale[n] : 0.0f;
         const float b = (nin && p.bias) ? p.bias[n] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RI; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int row = wm * 64 + i * 16 + 4 * g + v;
+            const int row = wm * (MROWS / 2) + i * 16 + 4 * g + v;
             const int64_t m = m0 + row;
             const bool min_ = m < M;
             const int xz = min_ ? p.xz[m] : 0;
@@ -325,15 +328,20 @@ hipError_t launch_one(const GemmArgs &a, int tiles_m, int tiles_n, hipStream_t s
 hipError_t launch_gemm_i8(const GemmArgs &a, GemmEpi epi, bool two_pass, hipStream_t st) {
   const int tiles_n = (int)((a.N + BN - 1) / BN);
   const int tiles_m128 = (int)((a.M + BM - 1) / BM), tiles_m64 = (int)((a.M + BM / 2 - 1) / (BM / 2));
+  // one pass: 64-row tiles while 128-row tiles would leave CUs idle (M = 512,
+  // N = K = 4096: 128 tiles of 128 rows; 27.3 -> 24.9 us for the static op)
+  const bool half = tiles_m128 * tiles_n < 256;
   switch (epi) {
-    case EPI_RAW: return launch_one<EPI_RAW, 0>(a, tiles_m128, tiles_n, st);
+    case EPI_RAW:
+      return half ? launch_one<EPI_RAW, 2>(a, tiles_m64, tiles_n, st)
+                  : launch_one<EPI_RAW, 0>(a, tiles_m128, tiles_n, st);
     case EPI_Q8TA:
       if (two_pass) return launch_one<EPI_Q8TA, 1>(a, tiles_m64, tiles_n, st);
-      // one pass: 64-row tiles while 128-row tiles would leave CUs idle
-      // (M = 512, N = K = 4096: 128 tiles of 128 rows)
-      if (tiles_m128 * tiles_n < 256) return launch_one<EPI_Q8TA, 2>(a, tiles_m64, tiles_n, st);
-      return launch_one<EPI_Q8TA, 0>(a, tiles_m128, tiles_n, st);
-    case EPI_DQ8: return launch_one<EPI_DQ8, 0>(a, tiles_m128, tiles_n, st);
+      return half ? launch_one<EPI_Q8TA, 2>(a, tiles_m64, tiles_n, st)
+                  : launch_one<EPI_Q8TA, 0>(a, tiles_m128, tiles_n, st);
+    case EPI_DQ8:
+      return half ? launch_one<EPI_DQ8, 2>(a, tiles_m64, tiles_n, st)
+                  : launch_one<EPI_DQ8, 0>(a, tiles_m128, tiles_n, st);
   }
   return hipErrorInvalidValue;
 }

@@ -174,8 +174,10 @@ def test_quantize_act_per_tensor(two_pass, M, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (17, 33, 80), (130, 257, 272), (256, 256, 4096),
-                                   (3, 500, 64)])
+                                   (3, 500, 64), (2050, 2100, 32)])
 def test_gemm_i8_i32(M, N, K):
+    """int32 stage entry: 64-row tiles while 128-row tiles would be fewer than
+    256, 128-row tiles from there (2050 x 2100: 17 x 17 of them)."""
     say("gemm_i8_i32", M, N, K)
     rng = np.random.default_rng(M * 7 + N + K)
     a = rng.integers(-128, 128, size=(M, K), dtype=np.int64).astype(np.int8)
@@ -443,7 +445,8 @@ def _dq8ca_case(x, w, wfmt, bias=None):
 
 @pytest.mark.parametrize("wfmt", [aql.AQL_W_Q8CSW, aql.AQL_W_Q4GSW])
 @pytest.mark.parametrize("M,N,K", [(1, 30, 64), (4, 100, 4096), (16, 17, 96), (17, 200, 256),
-                                   (128, 129, 512), (200, 64, 160), (40, 33, 32), (17, 1, 64)])
+                                   (128, 129, 512), (200, 64, 160), (40, 33, 32), (17, 1, 64),
+                                   (2050, 2100, 64)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_dq8ca_shapes(wfmt, M, N, K, with_bias):
     say("dq8ca", wfmt, M, N, K, with_bias)

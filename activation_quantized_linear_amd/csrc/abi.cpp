@@ -231,7 +231,9 @@ size_t aql_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
     return aql::gptq_workspace_bytes(N, K, M);
   }
   if (op == AQL_OP_W8A16) {
-    if (M < kW8A16GemmMinM || K > (1LL << 22) || N == 0) return 0;
+    if (N == 0 || K > kMaxKW8A16) return 0;
+    if (M < kW8A16GemmMinM) return aql::w8a16_skinny_part_bytes(M, N, K);
+    if (K > (1LL << 22)) return 0;
     return aql::w8a16_gemm_part_bytes(M, N, K);
   }
   return 0;
@@ -327,7 +329,9 @@ int aql_linear_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
     return launched(aql::launch_w8a16_gemm(x, M, K, q, scale, bias, N, y, static_cast<float *>(ws),
                                            ws ? ws_bytes : 0, (hipStream_t)stream),
                     fn);
-  return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, (hipStream_t)stream), fn);
+  return launched(aql::launch_w8a16(x, M, K, q, scale, bias, N, y, static_cast<float *>(ws),
+                                    ws ? ws_bytes : 0, (hipStream_t)stream),
+                  fn);
 }
 
 size_t aql_w8a16_group_table_bytes(int count) {

@@ -7,9 +7,18 @@
 
 namespace aql {
 
+// part (may be null): device memory for split-K partial sums; with at least
+// w8a16_skinny_part_bytes(M, N, K) bytes the shapes that split do so.
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
-                        hipStream_t st);
+                        float *part, size_t part_bytes, hipStream_t st);
+
+// K splits of the shared-x skinny tile below kW8A16ShareMinN channels (1: the
+// shape does not split): 12 <= M < 64, K >= 8192, 4 splits up to 128 tiles of
+// 64 channels x 16 rows, 2 up to 256, so the grid fills the CUs. The fp32
+// partial sums then need w8a16_skinny_part_bytes(M, N, K) bytes.
+int w8a16_skinny_splits(int64_t M, int64_t N, int64_t K);
+size_t w8a16_skinny_part_bytes(int64_t M, int64_t N, int64_t K);
 
 // Single-row GEMV over contiguous 1 KB row pieces, used by launch_w8a16 for
 // M = 1 and kW8A16ContigMinK <= K <= kW8A16ContigMaxK (measured faster than the

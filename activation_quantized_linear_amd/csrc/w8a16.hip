@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "w8a16.h"
+#include "w8a16_gemm.h"
 
 namespace aql {
 namespace {
@@ -1014,12 +1015,15 @@ struct ShLds {
   f32x4 red[WC * WK][64];
 };
 
+// part == nullptr: the whole K, y written. Else split blockIdx.z takes steps
+// [z spl, (z + 1) spl) and writes its unscaled sums to part[z][M][N] (fp32).
 template <int WC, int WK>
 __global__ __launch_bounds__(64 * WC * WK) void k_w8a16_sksh(const uint16_t *__restrict__ x, int64_t M,
                                                              int64_t K, const int8_t *__restrict__ q,
                                                              const float *__restrict__ scale,
                                                              const uint16_t *__restrict__ bias,
-                                                             int64_t N, uint16_t *__restrict__ y) {
+                                                             int64_t N, uint16_t *__restrict__ y,
+                                                             float *__restrict__ part, int spl) {
   static_assert(8 % WC == 0, "x pieces split over a range's waves");
   __shared__ __attribute__((aligned(16))) ShLds<WC, WK> sm;
   const int lane = threadIdx.x & 63;
@@ -1033,9 +1037,11 @@ __global__ __launch_bounds__(64 * WC * WK) void k_w8a16_sksh(const uint16_t *__r
   const __amdgpu_buffer_rsrc_t rq = rsrc(nrows > 0 ? q + n0 * K : q, (uint32_t)(nrows * K));
   const __amdgpu_buffer_rsrc_t rx = rsrc(x + m0 * K, (uint32_t)(mrows * K * 2));
   const int nst = (int)((K + 255) >> 8);
-  // range wk takes steps wk, wk + WK, ...; every wave runs the same number of
-  // steps (for the barriers), steps past its range load zeros
-  const int cnt = (nst + WK - 1) / WK;
+  const int s0 = part ? (int)blockIdx.z * spl : 0;
+  const int s1 = part ? (s0 + spl < nst ? s0 + spl : nst) : nst;
+  // range wk takes steps s0 + wk, s0 + wk + WK, ...; every wave runs the same
+  // number of steps (for the barriers), steps past its range load zeros
+  const int cnt = (s1 - s0 + WK - 1) / WK;
   const int drow = lane >> 4, dslot = lane & 15;
   const uint32_t lw0 = (uint32_t)(uintptr_t)&sm.w[wave][0][0];
   const uint32_t lx0 = (uint32_t)(uintptr_t)&sm.x[wk][0][0];
@@ -1044,8 +1050,8 @@ __global__ __launch_bounds__(64 * WC * WK) void k_w8a16_sksh(const uint16_t *__r
   constexpr int XP = 8 / WC;  // x pieces a wave copies per step
   constexpr int NV = 4 + XP;  // vector memory instructions per step and wave
   auto fetch = [&](int i, int slot) {
-    const int st = wk + WK * i;
-    const bool valid = st < nst;  // uniform
+    const int st = s0 + wk + WK * i;
+    const bool valid = st < s1;  // uniform
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int row = 4 * d + drow;
@@ -1123,6 +1129,14 @@ __global__ __launch_bounds__(64 * WC * WK) void k_w8a16_sksh(const uint16_t *__r
   }
   const int64_t n = n0 + r;
   if (n >= N) return;
+  if (part) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mm = m0 + 4 * g + v;
+      if (mm < M) part[((int64_t)blockIdx.z * M + mm) * N + n] = acc[v];
+    }
+    return;
+  }
   const float s = scale[n];
   const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
 #pragma unroll
@@ -1386,9 +1400,20 @@ hipError_t launch_w8a16_mfew(const uint16_t *x, int64_t M, int64_t K, const int8
   return hipGetLastError();
 }
 
+int w8a16_skinny_splits(int64_t M, int64_t N, int64_t K) {
+  if (M < 12 || M >= 64 || N >= kW8A16ShareMinN || K < 8192) return 1;
+  const int64_t tiles = ((N + 63) / 64) * ((M + 15) / 16);
+  return tiles <= 128 ? 4 : tiles <= 256 ? 2 : 1;
+}
+
+size_t w8a16_skinny_part_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = w8a16_skinny_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * 4 : 0;
+}
+
 hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q,
                         const float *scale, const uint16_t *bias, int64_t N, uint16_t *y,
-                        hipStream_t st) {
+                        float *part, size_t part_bytes, hipStream_t st) {
   if (M == 1 && K >= kW8A16ContigMinK && K <= kW8A16ContigMaxK)
     return launch_w8a16_m1c(x, K, q, scale, bias, N, y, st);
   if (M >= 2 && M <= kW8A16FewMaxM && K >= kW8A16FewMinK && K <= kW8A16FewMaxK)
@@ -1400,10 +1425,25 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, int64_t K, const int8_t *q
     // K = N = 8192: 20.0 vs 22.4)
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16));
     if (N >= 12288 && K <= 4096)
-      hipLaunchKernelGGL((k_w8a16_sksh<4, 1>), grid, dim3(256), 0, st, x, M, K, q, scale, bias, N, y);
+      hipLaunchKernelGGL((k_w8a16_sksh<4, 1>), grid, dim3(256), 0, st, x, M, K, q, scale, bias, N, y, nullptr, 0);
     else
-      hipLaunchKernelGGL((k_w8a16_sksh<4, 2>), grid, dim3(512), 0, st, x, M, K, q, scale, bias, N, y);
+      hipLaunchKernelGGL((k_w8a16_sksh<4, 2>), grid, dim3(512), 0, st, x, M, K, q, scale, bias, N, y, nullptr, 0);
     return hipGetLastError();
+  }
+  const int S = w8a16_skinny_splits(M, N, K);
+  if (S > 1 && part && part_bytes >= w8a16_skinny_part_bytes(M, N, K)) {
+    // Fewer channels: the shared-x form over S ranges of K, each writing its
+    // fp32 partial sums, then their sum (M = 16, K = 14336, N = 4096: 16.4 us
+    // against 19.1 for the skinny tile; M = 32: 20.5 vs 32.3; rotated weights)
+    const int nst = (int)((K + 255) / 256);
+    const int spl = (nst + S - 1) / S;
+    const int splits = (nst + spl - 1) / spl;
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16), (unsigned)splits);
+    hipLaunchKernelGGL((k_w8a16_sksh<4, 1>), grid, dim3(256), 0, st, x, M, K, q, scale, bias, N, y,
+                       part, spl);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_w8a16_splitk_reduce(part, splits, M, N, scale, bias, y, st);
   }
   return launch_w8a16_shape(w8a16_shape(M, N, K), x, M, K, q, scale, bias, N, y, st);
 }

@@ -14,6 +14,12 @@ namespace aql {
 int w8a16_gemm_splits(int64_t M, int64_t N, int64_t K);
 size_t w8a16_gemm_part_bytes(int64_t M, int64_t N, int64_t K);
 
+// y[m, n] = bf16(scale[n] (part[0][m][n] + ... + part[S-1][m][n]) + bias[n]),
+// the partial sums (fp32, S x M x N) added in split order.
+hipError_t launch_w8a16_splitk_reduce(const float *part, int S, int64_t M, int64_t N,
+                                      const float *scale, const uint16_t *bias, uint16_t *y,
+                                      hipStream_t st);
+
 // y[M, N] bf16 = scale[n] * x[M, K] bf16 . q[N, K]^T int8 (+ bias[n] bf16);
 // K <= 2^22 (32-bit buffer offsets of a 128-row tile of x). part (may be
 // null): device memory for the split-K partial sums; with at least

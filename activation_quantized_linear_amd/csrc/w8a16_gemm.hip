@@ -632,6 +632,19 @@ __global__ __launch_bounds__(256) void k_w8a16_splitk_reduce(const float *__rest
   }
 }
 
+}  // namespace
+
+hipError_t launch_w8a16_splitk_reduce(const float *part, int S, int64_t M, int64_t N,
+                                      const float *scale, const uint16_t *bias, uint16_t *y,
+                                      hipStream_t st) {
+  const int64_t groups = M * ((N + 3) / 4);
+  hipLaunchKernelGGL(k_w8a16_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     st, part, S, M, N, scale, bias, y);
+  return hipGetLastError();
+}
+
+namespace {
+
 template <int SG>
 hipError_t launch_wide(const uint16_t *x, int64_t M, int64_t K, const int8_t *q, const float *scale,
                        const uint16_t *bias, int64_t N, uint16_t *y, hipStream_t st) {
@@ -670,10 +683,7 @@ hipError_t launch_wide_split(const uint16_t *x, int64_t M, int64_t K, const int8
   hipLaunchKernelGGL((k_w8a16_gemm_wide<SG, true>), dim3((unsigned)(tiles_m * tiles_n * splits)),
                      dim3(512), L::BYTES_SPLIT, st, x, q, scale, bias, y, M, N, K, tiles_m,
                      tiles_n, part, ks);
-  const int64_t groups = M * ((N + 3) / 4);
-  hipLaunchKernelGGL(k_w8a16_splitk_reduce, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
-                     st, part, splits, M, N, scale, bias, y);
-  return hipGetLastError();
+  return launch_w8a16_splitk_reduce(part, splits, M, N, scale, bias, y, st);
 }
 
 template <int WM, int TI, int SG, int KP, bool RAG>

@@ -345,7 +345,7 @@ def sec_llm7b(torch, aql, workloads, dev):
                 fn(i)
             if M <= 16:  # short calls: the C entry point with prebuilt arguments
                 fn = raw_call(aql, torch, "aql_linear_w8a16",
-                              [(x, M, K, qs[i], s, None, N, y, None, 0) for i in range(ncopy)])
+                              [(x, M, K, qs[i], s, None, N, y, wsb, nws) for i in range(ncopy)])
             med, _ = event_time_ms(torch, fn, 50 if M <= 16 else 10, ncopy,
                                    warm_ms=0.0 if M <= 16 else 40.0)
             nb = N * K + 4 * N + 2 * M * K + 2 * M * N

@@ -191,10 +191,11 @@ int aql_quantize_act_per_tensor(const float *x, int64_t M, int64_t K, float s1, 
  *   y      device, [M, N] bf16, fp32 accumulate, round-to-nearest-even (output)
  *   ws     device workspace (may be NULL). With at least
  *          aql_workspace_bytes(AQL_OP_W8A16, M, N, K) bytes (nonzero only for
- *          prefill shapes of few output tiles and long rows), the tiled kernel
- *          splits K over more workgroups and adds their fp32 partial sums in a
- *          second launch; otherwise, or with a smaller workspace, it does not.
- *          The result is the same up to the order of the fp32 additions.
+ *          shapes of few output tiles and long rows: prefill, and 12 <= M < 64
+ *          with fewer than 8192 channels and K >= 8192), the kernel splits K
+ *          over more workgroups and adds their fp32 partial sums in a second
+ *          launch; otherwise, or with a smaller workspace, it does not. The
+ *          result is the same up to the order of the fp32 additions.
  * Errors: NULL x/q/scale/y (M, N > 0); M, N < 0; K < 16 or K % 16 != 0;
  * misaligned pointers (ws included).
  */

@@ -113,7 +113,9 @@ def test_w8a16_validation():
 def test_w8a16_workspace_bytes():
     """The optional split-K workspace: S x M x N floats for prefill shapes of
     few 128 x 256 tiles and K >= 8192 (S doubles while the units stay <= 256
-    and each keeps >= 16 stages of 64 k), 0 elsewhere."""
+    and each keeps >= 16 stages of 64 k), and for 12 <= M < 64 rows with fewer
+    than 8192 channels and K >= 8192 (4 splits up to 128 tiles of 64 channels
+    x 16 rows, 2 up to 256); 0 elsewhere."""
     wb = lambda M, N, K: L.aql_workspace_bytes(aql.AQL_OP_W8A16, M, N, K)
     assert wb(512, 4096, 14336) == 4 * 512 * 4096 * 4    # 64 tiles -> 4 splits
     assert wb(1024, 4096, 14336) == 2 * 1024 * 4096 * 4  # 128 tiles -> 2
@@ -121,7 +123,15 @@ def test_w8a16_workspace_bytes():
     assert wb(64, 300, 16384) == 16 * 64 * 300 * 4
     assert wb(2048, 4096, 14336) == 0                    # 256 wide tiles: no split
     assert wb(512, 14336, 4096) == 0                     # K < 8192
-    assert wb(16, 4096, 14336) == 0                      # decode band
+    assert wb(16, 4096, 14336) == 4 * 16 * 4096 * 4      # 64 skinny tiles -> 4
+    assert wb(32, 4096, 11008) == 4 * 32 * 4096 * 4      # 128 -> 4
+    assert wb(48, 5000, 8192) == 2 * 48 * 5000 * 4       # 237 -> 2
+    assert wb(63, 8000, 8192) == 0                       # 500 tiles: no split
+    assert wb(11, 4096, 14336) == 0                      # M < 12: the skinny tile
+    assert wb(16, 8192, 14336) == 0                      # 8192 channels: shared-x form
+    assert wb(16, 4096, 8176) == 0                       # K < 8192
+    assert wb(1, 4096, 14336) == 0                       # decode band
+    assert wb(4, 4096, 14336) == 0
     assert wb(512, 4096, -1) == 0
 
 

@@ -339,6 +339,30 @@ def test_w8a16_prefill_split_k(M, N, K):
         check_float(host(y.float()), yref, tol, BF16, f"w8a16 split-K {M}x{N}x{K} ws={nbytes}")
 
 
+@pytest.mark.parametrize("M,N,K", [(12, 1000, 8192), (40, 4100, 9008), (63, 2052, 16400),
+                                   (13, 70, 65536), (16, 4096, 14336)])
+def test_w8a16_skinny_split_k(M, N, K):
+    """12 <= M < 64, fewer than 8192 channels and long rows: with a workspace
+    the shared-x skinny tile splits K (4 ranges up to 128 tiles of 64 x 16, 2
+    up to 256; a last range shorter than the others, a last 256-k step partly
+    past K, ragged rows and channels) and a second launch adds the partial
+    sums; with a workspace below the size asked for, the same call runs the
+    skinny tile. Both against the oracle."""
+    say("w8a16 skinny split-K", M, N, K)
+    nb = aql.aql_workspace_bytes(aql.AQL_OP_W8A16, M, N, K)
+    assert nb > 0
+    g = workloads.gen(770 + M + N + K)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, M, K).to(torch.bfloat16)
+    b = workloads.small_matrix(g, 1, N)[0].to(torch.bfloat16)
+    q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+    yref, tol = oracle.linear_w8a16(bits(x), host(q), host(s), bits(b))
+    for nbytes in (nb, 16):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+        y = aql.aql_linear_w8a16(dev(x), q, s, dev(b), workspace=ws)
+        check_float(host(y.float()), yref, tol, BF16, f"w8a16 skinny split-K {M}x{N}x{K} ws={nbytes}")
+
+
 @pytest.mark.parametrize("K,N", list(workloads.LLM7B_SHAPES))
 @pytest.mark.parametrize("M", [512, 2048])
 def test_w8a16_llm7b_prefill_full_size(K, N, M):

@@ -445,8 +445,11 @@ int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *str
   sh.cgroups = h->cgroups;
   sh.xlds = h->xlds;
   if (pieces)
-    return launched(aql::launch_w8a16_m1p_grouped(dev_entries, h->count, h->total_blocks,
-                                                  (hipStream_t)stream),
+    return launched(aql::launch_w8a16_m1p_grouped(
+                        dev_entries,
+                        reinterpret_cast<const aql::W8A16GroupEntry *>(
+                            static_cast<const char *>(table) + sizeof(GroupHeader)),
+                        h->count, h->total_blocks, (hipStream_t)stream),
                     fn);
   return launched(aql::launch_w8a16_grouped(dev_entries, h->count, h->total_blocks, sh,
                                             (hipStream_t)stream),

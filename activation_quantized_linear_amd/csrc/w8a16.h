@@ -79,6 +79,12 @@ struct W8A16GroupEntry {
 };
 static_assert(sizeof(W8A16GroupEntry) == 80, "table layout");
 
+// Small groups travel by value in the kernel arguments.
+constexpr int kW8A16InlineMax = 4;
+struct W8A16InlineGroup {
+  W8A16GroupEntry e[kW8A16InlineMax];
+};
+
 hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
                                 const W8A16Shape &sh, hipStream_t st);
 
@@ -89,7 +95,9 @@ hipError_t launch_w8a16_grouped(const W8A16GroupEntry *dev_tab, int count, int t
 constexpr int64_t kW8A16PiecesMinK = 768;
 constexpr int64_t kW8A16PiecesMaxK = 4096;
 constexpr int64_t w8a16_pieces_tile_channels(int64_t K) { return K > 1024 ? 8 : 32; }
-hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
-                                    hipStream_t st);
+// host_tab (may be NULL): the same entries in host memory; a group of at most
+// kW8A16InlineMax entries then goes by value in the kernel arguments
+hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, const W8A16GroupEntry *host_tab,
+                                    int count, int total_blocks, hipStream_t st);
 
 }  // namespace aql

@@ -669,22 +669,12 @@ __global__ __launch_bounds__(64 * W) void k_w8a16_m1c(const uint16_t *__restrict
 // of 256. x comes straight from memory (the waves of a workgroup read the
 // same bytes of it, which the L1 serves) into fp32 registers.
 template <int B>
-__global__ __launch_bounds__(256) void k_w8a16_m1p_grouped(const W8A16GroupEntry *__restrict__ tab,
-                                                           int count) {
+__device__ __forceinline__ void m1p_body(const W8A16GroupEntry &e, int local) {
   constexpr int W = 4, R = 8, NB = (R + B - 1) / B;
   __shared__ float red[W][R];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int blk = blockIdx.x;
-  int lo = 0, hi = count - 1;
-  while (lo < hi) {  // last entry with begin <= blk
-    const int mid = (lo + hi + 1) >> 1;
-    if (tab[mid].blk_begin <= blk) lo = mid;
-    else hi = mid - 1;
-  }
-  const W8A16GroupEntry &e = tab[lo];
   const int64_t K = e.K, N = e.N;
-  const int local = blk - e.blk_begin;
   const bool split = K > 1024;  // uniform
   const int64_t n0 = split ? (int64_t)local * R : ((int64_t)local * W + wave) * R;
   const int64_t k0 = split ? 1024LL * wave : 0;
@@ -779,6 +769,36 @@ __global__ __launch_bounds__(256) void k_w8a16_m1p_grouped(const W8A16GroupEntry
   if (n >= N) return;
   const float bv = e.bias ? bf16_to_f32(e.bias[n]) : 0.0f;
   e.y[n] = f32_to_bf16_rne(e.scale[n] * sum + bv);
+}
+
+template <int B>
+__global__ __launch_bounds__(256) void k_w8a16_m1p_grouped(const W8A16GroupEntry *__restrict__ tab,
+                                                           int count) {
+  const int blk = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {  // last entry with begin <= blk
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab[mid].blk_begin <= blk) lo = mid;
+    else hi = mid - 1;
+  }
+  const W8A16GroupEntry &e = tab[lo];
+  m1p_body<B>(e, blk - e.blk_begin);
+}
+
+// The same for a group of at most kW8A16InlineMax problems whose entries come
+// by value in the kernel arguments: the workgroup picks its entry with uniform
+// selects and issues its weight loads without first reading a table from
+// memory (two dependent round trips that a launch of a few MB, as in a decode
+// step whose launches wait on each other, would otherwise pay before its
+// weight stream starts).
+template <int B, int NI>
+__global__ __launch_bounds__(256) void k_w8a16_m1p_inline(W8A16InlineGroup g) {
+  const int blk = blockIdx.x;
+  W8A16GroupEntry e = g.e[0];
+#pragma unroll
+  for (int i = 1; i < NI; ++i)
+    if (g.e[i].blk_begin <= blk) e = g.e[i];
+  m1p_body<B>(e, blk - e.blk_begin);
 }
 
 // A few rows of x (2 <= M <= 4), contiguous form: the pieces and the wave
@@ -1363,16 +1383,30 @@ hipError_t launch_w8a16_m1c(const uint16_t *x, int64_t K, const int8_t *q, const
   // 4 waves split K, each with one or two pieces of 1 KB per row; one piece
   // per row is consumed in batches of 2 loads (K = 4096, N = 14336: 10.66 us
   // against 10.81 with batches of 4; a single launch of the read-only probe
-  // over the same 58.7 MB takes 10.39 us)
-  if (K <= 4096)
+  // over the same 58.7 MB takes 10.39 us). A grid of at most one workgroup a
+  // CU is bound by latency, not by the stream: its 8 loads go out at once.
+  if (K <= 4096 && grid.x <= 256)
+    hipLaunchKernelGGL((k_w8a16_m1c<4, 1, 8>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
+  else if (K <= 4096)
     hipLaunchKernelGGL((k_w8a16_m1c<4, 1, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
   else
     hipLaunchKernelGGL((k_w8a16_m1c<4, 2>), grid, dim3(256), 0, st, x, K, q, scale, bias, N, y);
   return hipGetLastError();
 }
 
-hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, int count, int total_blocks,
-                                    hipStream_t st) {
+hipError_t launch_w8a16_m1p_grouped(const W8A16GroupEntry *dev_tab, const W8A16GroupEntry *host_tab,
+                                    int count, int total_blocks, hipStream_t st) {
+  if (host_tab && count >= 1 && count <= kW8A16InlineMax) {
+    W8A16InlineGroup g = {};
+    for (int i = 0; i < count; ++i) g.e[i] = host_tab[i];
+    switch (count) {
+      case 1: hipLaunchKernelGGL((k_w8a16_m1p_inline<4, 1>), dim3((unsigned)total_blocks), dim3(256), 0, st, g); break;
+      case 2: hipLaunchKernelGGL((k_w8a16_m1p_inline<4, 2>), dim3((unsigned)total_blocks), dim3(256), 0, st, g); break;
+      case 3: hipLaunchKernelGGL((k_w8a16_m1p_inline<4, 3>), dim3((unsigned)total_blocks), dim3(256), 0, st, g); break;
+      default: hipLaunchKernelGGL((k_w8a16_m1p_inline<4, 4>), dim3((unsigned)total_blocks), dim3(256), 0, st, g); break;
+    }
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_w8a16_m1p_grouped<4>), dim3((unsigned)total_blocks), dim3(256), 0, st,
                      dev_tab, count);
   return hipGetLastError();

@@ -322,7 +322,11 @@ int aql_w8a16_group_plan(const aql_w8a16_problem *problems, int count, void *tab
 /* Run a planned group. table: the host table written by aql_w8a16_group_plan;
  * dev_table: its device copy (16-byte aligned). Errors: table not written by
  * the plan function (AQL_ERR_PARAM), dev_table NULL or misaligned. A group
- * whose problems are all empty returns AQL_OK without launching. */
+ * whose problems are all empty returns AQL_OK without launching. A
+ * single-row group of at most 4 problems whose K all lie in the range of the
+ * contiguous-pieces kernel takes its entries from the host table at launch
+ * (they travel in the kernel arguments); larger groups read dev_table when
+ * the kernel runs. Both tables must describe the same plan. */
 int aql_linear_w8a16_grouped(const void *table, const void *dev_table, void *stream);
 
 /* ------------------------------------------------------------ stage entry */

@@ -261,6 +261,50 @@ def test_w8a16_grouped_pieces_ragged(dense):
         check_float(host(y.float()), yref, tol, BF16, f"pieces ragged {tuple(q.shape)}")
 
 
+@pytest.mark.parametrize("count", [1, 2, 3, 4, 5])
+def test_w8a16_grouped_pieces_small_groups(count):
+    """Groups of at most 4 problems go to the pieces kernel by value in the
+    kernel arguments (a group of 5 reads its table from memory): each workgroup
+    must pick its own problem, including the last block of a ragged N and
+    problems with K above and below one 1 KB piece."""
+    g = workloads.gen(730 + count)
+    pool = [(2570, 960), (9, 2560), (1, 1040), (41, 4096), (960, 768)]
+    shapes = pool[:count]
+    probs, refs = [], []
+    for N, K in shapes:
+        w = workloads.small_matrix(g, N, K, std=0.02)
+        x = workloads.small_matrix(g, 1, K).to(torch.bfloat16)
+        q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+        b = workloads.small_matrix(g, 1, N).to(torch.bfloat16)[0]
+        y = torch.full((1, N), float("nan"), dtype=torch.bfloat16, device=DEV)
+        probs.append((dev(x), q, s, dev(b), y))
+        refs.append((x, b))
+    host_t, dev_t = aql.aql_w8a16_group_plan(probs)
+    h = _plan_header(host_t)
+    say("pieces small group", count, h)
+    assert h["kind"] == 1 and h["count"] == count
+    aql.aql_linear_w8a16_grouped(host_t, dev_t)
+    for (x, q, s, _, y), (xc, bc) in zip(probs, refs):
+        yref, tol = oracle.linear_w8a16(bits(xc), host(q), host(s), bits(bc))
+        check_float(host(y.float()), yref, tol, BF16, f"small group {count} {tuple(q.shape)}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 2048), (9, 2560), (960, 2560), (2048, 4096), (2049, 4096),
+                                 (1000, 3000 // 16 * 16)])
+def test_w8a16_single_row_contiguous_small_grids(N, K):
+    """The contiguous single-row GEMV at grids of at most one workgroup a CU
+    (all 8 weight loads of a wave in flight at once) and just past it (N =
+    2049: batches of 2)."""
+    g = workloads.gen(740 + N)
+    w = workloads.small_matrix(g, N, K, std=0.02)
+    x = workloads.small_matrix(g, 1, K).to(torch.bfloat16)
+    say("m1c small grid", N, K)
+    q, s, _ = aql.aql_quantize_weight_int8(dev(w), aql.AQL_WQ_SYM127)
+    y = host(aql.aql_linear_w8a16(dev(x), q, s, None).float())
+    yref, tol = oracle.linear_w8a16(bits(x), host(q), host(s), None)
+    check_float(y, yref, tol, BF16, f"m1c small grid N={N} K={K}")
+
+
 def test_w8a16_grouped_paired_tiles_ragged_n():
     """A single-row group past 8,192 wave tiles (so tiles are paired per
     workgroup) whose channel counts leave the second tile of a pair partly

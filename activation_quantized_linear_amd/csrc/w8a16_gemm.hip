@@ -605,14 +605,27 @@ __global__ __launch_bounds__(256) void k_w8a16_splitk_reduce(const float *__rest
   const int cnt = N - n < 4 ? (int)(N - n) : 4;
   const bool vec = (N & 3) == 0;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < S; ++s) {
-    const float *src = part + ((int64_t)s * M + m) * N + n;
-    if (vec) {
-      acc += *reinterpret_cast<const f32x4 *>(src);
-    } else {
+  if (vec && S <= 4) {
+    // all the splits' loads in flight before the first add (same order of sums)
+    f32x4 v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < cnt) acc[e] += src[e];
+    for (int s = 0; s < 4; ++s)
+      v[s] = s < S ? __builtin_nontemporal_load(
+                         reinterpret_cast<const f32x4 *>(part + ((int64_t)s * M + m) * N + n))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (s < S) acc += v[s];
+  } else {
+    for (int s = 0; s < S; ++s) {
+      const float *src = part + ((int64_t)s * M + m) * N + n;
+      if (vec) {
+        acc += *reinterpret_cast<const f32x4 *>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < cnt) acc[e] += src[e];
+      }
     }
   }
   uint16_t out[4];

@@ -443,6 +443,7 @@ using QTM = QT<4, 4, 1, 1, 4, 3, 4>;  // 64 x 64
 using QTN = QT<4, 3, 1, 1, 4, 3, 4>;  // 64 x 48
 using QTP = QT<2, 3, 1, 2, 4, 3, 4>;  // 32 x 96
 using QTR = QT<2, 3, 1, 1, 4, 3, 4>;  // 32 x 48
+using QTQ = QT<4, 3, 1, 2, 4, 3, 4>;  // 64 x 96
 
 __device__ __forceinline__ bf16x8 bf16x8_splat(uint32_t bits) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -825,11 +826,19 @@ hipError_t launch_dq8ca_q4(const Q4Args &a, hipStream_t st) {
     // two waves), 32 x 96 up to M = 64 (19.6 vs 20.9 for 32 x 48), 64 x 48 up
     // to M = 256 (29.7 vs 37.8 at M = 128, 47.1 vs 56.6 at M = 200) and
     // 64 x 64 above (58.2 vs 67.8 at M = 300)
+    // 64 x 96 where its tiles fit one round of the 256 CUs and those of 64 x 48
+    // do not, the last row tile at least half full (M = 128: 31.2 vs 33.3 us;
+    // M = 96 30.3 vs 30.4; M = 80 29.7 vs 29.2; M = 160-200, two rounds of
+    // 64 x 96, 54-55 vs 48-52)
     const int64_t tl = ((a.M + QTL::BM - 1) / QTL::BM) * ((a.N + QTL::BN - 1) / QTL::BN);
+    const int64_t rt = (a.M + 63) / 64;
+    const bool q96 = rt * ((a.N + QTN::BN - 1) / QTN::BN) > 256 &&
+                     rt * ((a.N + QTQ::BN - 1) / QTQ::BN) <= 256 && (a.M % 64 == 0 || a.M % 64 >= 32);
     if (tl >= 640) launch_tiled<QTL>(a, st);
     else if (a.M >= 384) launch_tiled<QTW>(a, st);
     else if (a.M <= 32) launch_tiled<QTR>(a, st);
     else if (a.M <= 64) launch_tiled<QTP>(a, st);
+    else if (q96) launch_tiled<QTQ>(a, st);
     else if (a.M <= 256) launch_tiled<QTN>(a, st);
     else launch_tiled<QTM>(a, st);
   }

@@ -520,13 +520,16 @@ def test_dq8ca_q4_few_rows(M, N, K, with_bias):
 
 @pytest.mark.parametrize("M,N,K", [(2600, 4100, 96), (2000, 4100, 96), (1000, 4100, 160),
                                    (50, 1000, 224), (33, 47, 4064), (30, 201, 4064),
-                                   (150, 1001, 160), (65, 11008, 4096), (300, 700, 96)])
+                                   (150, 1001, 160), (65, 11008, 4096), (300, 700, 96),
+                                   (100, 7000, 1056), (128, 9650, 224), (80, 11008, 96)])
 def test_dq8ca_q4_large_tiles_ragged(M, N, K):
     """Each tile shape of the 4-bit tiled kernel with ragged edges in M and N
-    and group counts that leave the last stage partly empty (K = 96, 160, 224
-    and 4064): 128 x 128 (2600 x 4100: 693 of them), 128 x 96 (2000 x 4100,
-    1000 x 4100), and with the groups over 4 waves 64 x 64 (300 x 700), 64 x 48
-    (65 <= M <= 256), 32 x 96 (33 <= M <= 64) and 32 x 48 (M <= 32)."""
+    and group counts that leave the last stage partly empty (K = 96, 160, 224,
+    1056 and 4064): 128 x 128 (2600 x 4100: 693 of them), 128 x 96 (2000 x 4100,
+    1000 x 4100), and with the groups over 4 waves 64 x 64 (300 x 700), 64 x 96
+    (100 x 7000, 128 x 9650: one round of tiles where 64 x 48 would need two),
+    64 x 48 (the rest of 65 <= M <= 256, 80 x 11008 with its last row tile a
+    quarter full), 32 x 96 (33 <= M <= 64) and 32 x 48 (M <= 32)."""
     say("dq8ca q4 large ragged", M, N, K)
     g = workloads.gen(650)
     x = _edge_rows(workloads.small_matrix(g, M, K))
